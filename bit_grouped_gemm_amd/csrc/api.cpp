@@ -1,0 +1,349 @@
+// C ABI of the MoE library: argument validation, workspace carving and kernel dispatch.
+// The operations and their sources are documented in moe_w4.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "moe_internal.h"
+#include "moe_w4.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool w4_ok(const moe_w4_t& w) {
+  return w.q && w.scale && w.bias && aligned(w.q, 16) && aligned(w.scale, 2) && aligned(w.bias, 2);
+}
+
+// Descriptor checks shared by every entry point.
+int check_desc(const moe_layer_desc_t* d) {
+  if (!d) return MOE_INVALID_ARG;
+  if (d->bits != 4 || d->group_size != 64 || d->renormalize != 1) return MOE_UNSUPPORTED;
+  if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->ffn <= 0 || d->shared_ffn < 0)
+    return MOE_INVALID_ARG;
+  if (d->hidden % 64 || d->ffn % 64 || d->shared_ffn % 64) return MOE_UNSUPPORTED;
+  if (d->num_experts > 1024 || d->top_k > 32 || d->top_k > d->num_experts) return MOE_UNSUPPORTED;
+  if (d->hidden > 16384 || d->ffn > 16384 || d->shared_ffn > 16384) return MOE_UNSUPPORTED;
+  if (!d->router_w || !aligned(d->router_w, 16)) return MOE_INVALID_ARG;
+  if (d->router_bias && !aligned(d->router_bias, 4)) return MOE_INVALID_ARG;
+  if (!w4_ok(d->gate) || !w4_ok(d->up) || !w4_ok(d->down)) return MOE_INVALID_ARG;
+  if (d->shared_ffn > 0) {
+    if (!w4_ok(d->sh_gate) || !w4_ok(d->sh_up) || !w4_ok(d->sh_down)) return MOE_INVALID_ARG;
+    if (!d->shared_gate_w || !aligned(d->shared_gate_w, 4)) return MOE_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+Dims dims_of(const moe_layer_desc_t* d, int T) {
+  return Dims{d->hidden, d->num_experts, d->top_k, d->ffn, d->shared_ffn, T};
+}
+
+int max_blocks(const Dims& d) {
+  const int TK = d.TK();
+  const int routed = (TK + kBlockM - 1) / kBlockM + (d.E < TK ? d.E : TK);
+  const int shared = d.Fs > 0 ? (d.T + kBlockM - 1) / kBlockM : 0;
+  return routed + shared;
+}
+
+// Every index into the grouped activations stays inside 32 bits.
+bool sizes_ok(const Dims& d) {
+  const int64_t rows = (int64_t)d.T * d.K + d.T;
+  int64_t w = d.H;
+  if (d.F > w) w = d.F;
+  if (d.Fs > w) w = d.Fs;
+  return rows * w < (int64_t(1) << 31) && (int64_t)d.T * d.K < (int64_t(1) << 30);
+}
+
+// Workspace regions for T tokens, in order of use.
+struct Layout {
+  size_t logits, rsplit, hist, topk_idx, topk_w, sgate;
+  size_t counts, offsets, sorted, slotpos, blocks, nblk;
+  size_t a, y;
+  size_t end_route, end_permute, end_no_y, total;
+};
+
+Layout layout_of(const Dims& d, int flags) {
+  Layout L{};
+  size_t o = 0;
+  const size_t TK = (size_t)d.T * d.K;
+  const int nchunks = (int)((TK + kChunkSlots - 1) / kChunkSlots);
+  L.logits = o;  o = align_up(o + (size_t)d.T * d.E * 4);
+  L.rsplit = o;  o = align_up(o + (size_t)3 * d.E * d.H * 2);
+  L.end_route = o;
+  L.hist = o;    o = align_up(o + (size_t)nchunks * (d.E + 1) * 4);
+  L.end_permute = o;
+  L.topk_idx = o; o = align_up(o + TK * 4);
+  L.topk_w = o;  o = align_up(o + TK * 4);
+  L.sgate = o;   o = align_up(o + (size_t)d.T * 4);
+  L.counts = o;  o = align_up(o + (size_t)d.E * 4);
+  L.offsets = o; o = align_up(o + (size_t)(d.E + 1) * 4);
+  L.sorted = o;  o = align_up(o + TK * 4);
+  L.slotpos = o; o = align_up(o + TK * 4);
+  L.blocks = o;  o = align_up(o + (size_t)max_blocks(d) * 16);
+  L.nblk = o;    o = align_up(o + 4);
+  L.a = o;       o = align_up(o + (TK * d.F + (size_t)d.T * d.Fs) * 2);
+  L.end_no_y = o;
+  L.y = o;
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) o = align_up(o + (TK + d.T) * d.H * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_HIP_ERROR; }
+
+bool use_decode(const Dims& d, int flags) {
+  return d.T <= kDecodeMaxT && !(flags & MOE_FLAG_FORCE_PREFILL) && d.F <= 512 && d.Fs <= 512 &&
+         (size_t)d.T * d.H * 2 <= 65536;
+}
+
+int run_route(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, int32_t* idx,
+              float* w, float* sgate, void* ws, const Layout& L, bool decode, hipStream_t s) {
+  float* logits = at<float>(ws, L.logits);
+  hipError_t e;
+  if (decode) {
+    e = launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
+  } else {
+    uint16_t* parts = at<uint16_t>(ws, L.rsplit);
+    e = launch_router_split(desc->router_w, d.E, d.H, parts, s);
+    if (e != hipSuccess) return MOE_HIP_ERROR;
+    e = launch_router_logits_mfma(x, parts, desc->router_bias, d.T, d.E, d.H, logits, s);
+  }
+  if (e != hipSuccess) return MOE_HIP_ERROR;
+  const float* wg = d.Fs > 0 ? desc->shared_gate_w : nullptr;
+  return hip_status(launch_topk(logits, x, wg, d.T, d.E, d.K, d.H, idx, w, sgate, s));
+}
+
+GemmParams gemm_params(const moe_layer_desc_t* desc, const Dims& d, int which, const void* in,
+                       const moe_plan_t* plan, const float* topk_w, const float* sgate,
+                       void* out) {
+  GemmParams p{};
+  p.blocks = reinterpret_cast<const int4*>(plan->blocks);
+  p.num_blocks = plan->num_blocks;
+  p.sorted_slots = plan->sorted_slots;
+  p.K = d.K;
+  p.E = d.E;
+  p.TK = d.TK();
+  p.topk_w = topk_w;
+  p.shared_gate = sgate;
+  p.out = out;
+  p.out_ld = d.H;
+  const uint16_t* a = static_cast<const uint16_t*>(in);
+  if (which == MOE_GEMM_GATE_UP) {
+    p.a_routed = p.a_shared = a;
+    p.kdim_routed = p.kdim_shared = d.H;
+    p.n_routed = d.F;
+    p.n_shared = d.Fs;
+    p.w0 = desc->gate;
+    p.w1 = desc->up;
+    p.sw0 = desc->sh_gate;
+    p.sw1 = desc->sh_up;
+  } else {
+    p.a_routed = a;
+    p.a_shared = a + (size_t)d.TK() * d.F;
+    p.kdim_routed = d.F;
+    p.kdim_shared = d.Fs > 0 ? d.Fs : 64;
+    p.n_routed = d.H;
+    p.n_shared = d.Fs > 0 ? d.H : 0;
+    p.w0 = p.w1 = desc->down;
+    p.sw0 = p.sw1 = desc->sh_down;
+  }
+  return p;
+}
+
+bool plan_ok(const moe_plan_t* p) {
+  return p && p->counts && p->offsets && p->sorted_slots && p->slot_pos && p->blocks &&
+         p->num_blocks && aligned(p->blocks, 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_INVALID_ARG: return "invalid argument";
+    case MOE_UNSUPPORTED: return "unsupported layer layout";
+    case MOE_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_HIP_ERROR: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_version(void) { return "moe_w4 1.0 gfx950"; }
+
+size_t moe_workspace_bytes(const moe_layer_desc_t* desc, int32_t T_max, int32_t flags) {
+  if (check_desc(desc) != MOE_OK || T_max < 0) return 0;
+  const Dims d = dims_of(desc, T_max);
+  if (!sizes_ok(d)) return 0;
+  return layout_of(d, flags).total;
+}
+
+int32_t moe_plan_max_blocks(const moe_layer_desc_t* desc, int32_t T) {
+  if (check_desc(desc) != MOE_OK || T < 0) return 0;
+  return max_blocks(dims_of(desc, T));
+}
+
+int moe_route(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, int32_t* topk_idx,
+              float* topk_w, float* shared_gate, int32_t* counts, void* workspace,
+              size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  if (!x || !aligned(x, 16) || !topk_idx || !topk_w || !counts || !workspace)
+    return MOE_INVALID_ARG;
+  if (d.Fs > 0 && !shared_gate) return MOE_INVALID_ARG;
+  const Layout L = layout_of(d, 0);
+  if (ws_bytes < L.end_route) return MOE_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_route(desc, d, x, topk_idx, topk_w, shared_gate, workspace, L, use_decode(d, 0), s);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_count(topk_idx, d.TK(), d.E, counts, s));
+}
+
+int moe_permute(const moe_layer_desc_t* desc, const int32_t* topk_idx, int32_t T,
+                const moe_plan_t* plan, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  if (!topk_idx || !plan_ok(plan) || !workspace) return MOE_INVALID_ARG;
+  const Layout L = layout_of(d, 0);
+  if (ws_bytes < L.end_permute) return MOE_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_permute(topk_idx, d, d.Fs > 0, at<int32_t>(workspace, L.hist), *plan,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void* in, int32_t T,
+                        const moe_plan_t* plan, const float* topk_w, const float* shared_gate,
+                        void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (which < MOE_GEMM_GATE_UP || which > MOE_GEMM_DOWN_COMBINE_ATOMIC || T < 0)
+    return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  if (!in || !aligned(in, 16) || !out || !aligned(out, 16) || !plan_ok(plan))
+    return MOE_INVALID_ARG;
+  const bool combine = which == MOE_GEMM_DOWN_COMBINE || which == MOE_GEMM_DOWN_COMBINE_ATOMIC;
+  if (combine && (!topk_w || (d.Fs > 0 && !shared_gate))) return MOE_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mb = max_blocks(d);
+  // Few tokens: the same bandwidth-bound GEMV kernels as moe_layer_forward's decode path.
+  if (use_decode(d, 0) && which == MOE_GEMM_GATE_UP)
+    return hip_status(launch_dec_gateup(d, *desc, static_cast<const uint16_t*>(in), *plan, mb,
+                                        static_cast<uint16_t*>(out), s));
+  if (use_decode(d, 0) && which == MOE_GEMM_DOWN_COMBINE)
+    return hip_status(launch_dec_down(d, *desc, static_cast<const uint16_t*>(in), *plan, topk_w,
+                                      shared_gate, static_cast<float*>(out), s));
+  if (which == MOE_GEMM_GATE_UP || which == MOE_GEMM_DOWN) {
+    const GemmParams p = gemm_params(desc, d, which, in, plan, nullptr, nullptr, out);
+    return hip_status(launch_gemm_w4(which == MOE_GEMM_GATE_UP ? kGateUp : kDownStore, p, mb, s));
+  }
+  if (which == MOE_GEMM_DOWN_COMBINE_ATOMIC) {
+    if (launch_fill_zero(static_cast<float*>(out), (size_t)d.T * d.H, s) != hipSuccess)
+      return MOE_HIP_ERROR;
+    const GemmParams p = gemm_params(desc, d, which, in, plan, topk_w, shared_gate, out);
+    return hip_status(launch_gemm_w4(kDownAtomic, p, mb, s));
+  }
+  const Layout L = layout_of(d, 0);
+  if (!workspace) return MOE_INVALID_ARG;
+  if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
+  float* y = at<float>(workspace, L.y);
+  const GemmParams p = gemm_params(desc, d, MOE_GEMM_DOWN, in, plan, nullptr, nullptr, y);
+  if (launch_gemm_w4(kDownStore, p, mb, s) != hipSuccess) return MOE_HIP_ERROR;
+  return hip_status(launch_combine(y, plan->slot_pos, topk_w,
+                                   d.Fs > 0 ? y + (size_t)d.TK() * d.H : nullptr, shared_gate, d,
+                                   static_cast<float*>(out), s));
+}
+
+int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* shared_y, const float* shared_gate, int32_t T,
+                float* out, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  if (!y_perm || !aligned(y_perm, 16) || !slot_pos || !topk_w || !out || !aligned(out, 16))
+    return MOE_INVALID_ARG;
+  if (d.Fs > 0 && (!shared_y || !aligned(shared_y, 16) || !shared_gate)) return MOE_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, slot_pos, topk_w, d.Fs > 0 ? shared_y : nullptr,
+                                   shared_gate, d, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
+                      void* workspace, size_t ws_bytes, int32_t flags, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0 || (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_FORCE_PREFILL))) return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  if (!x || !aligned(x, 16) || !out || !aligned(out, 16) || !workspace) return MOE_INVALID_ARG;
+  const Layout L = layout_of(d, flags);
+  if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool decode = use_decode(d, flags);
+
+  int32_t* idx = at<int32_t>(workspace, L.topk_idx);
+  float* w = at<float>(workspace, L.topk_w);
+  float* sgate = at<float>(workspace, L.sgate);
+  moe_plan_t plan{at<int32_t>(workspace, L.counts), at<int32_t>(workspace, L.offsets),
+                  at<int32_t>(workspace, L.sorted),  at<int32_t>(workspace, L.slotpos),
+                  at<int32_t>(workspace, L.blocks),  at<int32_t>(workspace, L.nblk)};
+  uint16_t* a = at<uint16_t>(workspace, L.a);
+  const int mb = max_blocks(d);
+
+  st = run_route(desc, d, x, idx, w, sgate, workspace, L, decode, s);
+  if (st != MOE_OK) return st;
+  if (launch_permute(idx, d, d.Fs > 0, at<int32_t>(workspace, L.hist), plan, s) != hipSuccess)
+    return MOE_HIP_ERROR;
+  if (decode) {
+    if (launch_dec_gateup(d, *desc, x, plan, mb, a, s) != hipSuccess) return MOE_HIP_ERROR;
+    return hip_status(launch_dec_down(d, *desc, a, plan, w, sgate, out, s));
+  }
+  const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);
+  if (launch_gemm_w4(kGateUp, pg, mb, s) != hipSuccess) return MOE_HIP_ERROR;
+  if (flags & MOE_FLAG_ATOMIC_COMBINE) {
+    if (launch_fill_zero(out, (size_t)d.T * d.H, s) != hipSuccess) return MOE_HIP_ERROR;
+    const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN_COMBINE_ATOMIC, a, &plan, w, sgate, out);
+    return hip_status(launch_gemm_w4(kDownAtomic, pd, mb, s));
+  }
+  float* y = at<float>(workspace, L.y);
+  const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN, a, &plan, nullptr, nullptr, y);
+  if (launch_gemm_w4(kDownStore, pd, mb, s) != hipSuccess) return MOE_HIP_ERROR;
+  return hip_status(launch_combine(y, plan.slot_pos, w,
+                                   d.Fs > 0 ? y + (size_t)d.TK() * d.H : nullptr, sgate, d, out, s));
+}
+
+int moe_debug_dequant_w4(const moe_w4_t* w, int32_t n_rows, int32_t Kin, int32_t mat,
+                         int32_t row, float* out_f32, uint16_t* out_bf16, void* stream) {
+  if (!w || !w4_ok(*w) || n_rows <= 0 || Kin <= 0 || mat < 0 || row < 0 || row >= n_rows)
+    return MOE_INVALID_ARG;
+  if (Kin % 64) return MOE_UNSUPPORTED;
+  if (!out_f32 && !out_bf16) return MOE_INVALID_ARG;
+  return hip_status(launch_debug_dequant(*w, n_rows, Kin, mat, row, out_f32, out_bf16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

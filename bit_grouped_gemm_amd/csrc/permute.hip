@@ -1,0 +1,158 @@
+// Token permutation into per-expert groups: histogram, exclusive scan, stable scatter and the
+// block map, all on the device with no host synchronisation.
+//
+// "Perplexity's Lily: A Breakthrough Local Inference Engine Tailored Exclusively for Apple
+// Silicon", section "How It Works: Prefill and Decode Strategies": the histogram and the
+// routing logic (prefix scan, scatter, block maps) stay inside one GPU submission, with no
+// CPU synchronisation between expert layers.
+//
+// Slots s = t*K + k are split into chunks of kChunkSlots. Pass 1 writes one histogram row per
+// chunk (plus a bin for invalid expert ids). Pass 2 (one workgroup) turns the rows into
+// per-chunk starting positions, the expert offsets and the block map. Pass 3 scatters each
+// chunk in slot order, so the result is stable: inside an expert, slots stay ascending.
+#include "moe_internal.h"
+
+namespace moe {
+
+// hist row c: [E] counts of chunk c, then hist[c][E] = invalid ids in chunk c.
+__global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ idx, int TK, int E,
+                                              int32_t* __restrict__ hist) {
+  __shared__ int h[1025];
+  for (int e = threadIdx.x; e <= E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kChunkSlots, s1 = min(TK, s0 + kChunkSlots);
+  for (int s = s0 + threadIdx.x; s < s1; s += 256) {
+    const int e = idx[s];
+    atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
+  }
+  __syncthreads();
+  int32_t* row = hist + (size_t)blockIdx.x * (E + 1);
+  for (int e = threadIdx.x; e <= E; e += 256) row[e] = h[e];
+}
+
+// Exclusive scan over a 1024-thread workgroup (wave scans, then a scan of wave totals).
+__device__ int block_exclusive_scan_1024(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int t = wave_tot[w];
+      wave_tot[w] = run;
+      run += t;
+    }
+    *total = run;
+  }
+  __syncthreads();
+  const int r = wave_tot[wave] + inc - v;
+  __syncthreads();  // wave_tot may be reused by the caller
+  return r;
+}
+
+// One workgroup of 1024 threads (E <= 1024). Converts hist rows to chunk starting positions in
+// place, and writes counts, offsets, the block map and num_blocks (-1 if any id was invalid).
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nchunks, int E,
+                                               int T, int K, int has_shared,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int4* __restrict__ blocks,
+                                               int32_t* __restrict__ num_blocks) {
+  __shared__ int wave_tot[16];
+  __shared__ int total_slots, total_blocks, bad;
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * (E + 1) + e];
+  if (threadIdx.x == 0) {
+    int b = 0;
+    for (int c = 0; c < nchunks; ++c) b += hist[(size_t)c * (E + 1) + E];
+    bad = b;
+  }
+  const int off = block_exclusive_scan_1024(e < E ? cnt : 0, wave_tot, &total_slots);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = off;
+    int run = off;
+    for (int c = 0; c < nchunks; ++c) {
+      int32_t* p = hist + (size_t)c * (E + 1) + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+  }
+  const int nb = (e < E) ? (cnt + kBlockM - 1) / kBlockM : 0;
+  const int boff = block_exclusive_scan_1024(nb, wave_tot, &total_blocks);
+  if (e == 0) offsets[E] = total_slots;
+  for (int j = 0; j < nb; ++j) {
+    const int m0 = j * kBlockM;
+    blocks[boff + j] = make_int4(e, m0, min(kBlockM, cnt - m0), off + m0);
+  }
+  const int TK = T * K;
+  const int nbs = has_shared ? (T + kBlockM - 1) / kBlockM : 0;
+  for (int j = threadIdx.x; j < nbs; j += 1024) {
+    const int m0 = j * kBlockM;
+    blocks[total_blocks + j] = make_int4(E, m0, min(kBlockM, T - m0), TK + m0);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *num_blocks = bad ? -1 : total_blocks + nbs;
+}
+
+// One wave per chunk. For 64 slots at a time, the lanes that hold the same expert are found
+// with one ballot per bit of the expert id; a lane's rank among its peers is the number of
+// lower peer lanes, and the lowest peer advances the expert's running position afterwards.
+__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ idx, int TK, int E,
+                                                int nbits, const int32_t* __restrict__ base,
+                                                int32_t* __restrict__ sorted_slots,
+                                                int32_t* __restrict__ slot_pos) {
+  __shared__ int cur[1024];
+  const int lane = threadIdx.x;
+  const int32_t* row = base + (size_t)blockIdx.x * (E + 1);
+  for (int e = lane; e < E; e += 64) cur[e] = row[e];
+  __syncthreads();
+  const int s0 = blockIdx.x * kChunkSlots, s1 = min(TK, s0 + kChunkSlots);
+  for (int sb = s0; sb < s1; sb += 64) {
+    const int s = sb + lane;
+    const int e = (s < s1) ? idx[s] : -1;
+    const bool ok = e >= 0 && e < E;
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t lower = peers & ((1ull << lane) - 1ull);
+    int p = 0;
+    if (ok) p = cur[e] + __popcll(lower);
+    __syncthreads();
+    if (ok && lower == 0) cur[e] += __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      sorted_slots[p] = s;
+      slot_pos[s] = p;
+    }
+  }
+}
+
+hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_t* hist,
+                          const moe_plan_t& plan, hipStream_t s) {
+  const int TK = d.TK();
+  const int nchunks = (TK + kChunkSlots - 1) / kChunkSlots;
+  int nbits = 0;
+  while ((1 << nbits) < d.E) ++nbits;
+  hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(256), 0, s, idx, TK, d.E, hist);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nchunks, d.E, d.T, d.K,
+                     shared ? 1 : 0, plan.counts, plan.offsets,
+                     reinterpret_cast<int4*>(plan.blocks), plan.num_blocks);
+  hipLaunchKernelGGL(k_scatter, dim3(nchunks), dim3(64), 0, s, idx, TK, d.E, nbits, hist,
+                     plan.sorted_slots, plan.slot_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,200 @@
+/*
+ * moe_w4.h - C ABI of the MI355X (gfx950) MoE-layer library: router, permutation,
+ * 4-bit group-64 grouped GEMM, combine, and the whole layer.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "Perplexity's Lily: A Breakthrough Local Inference Engine Tailored Exclusively for
+ *        Apple Silicon", sections "The Model: Qwen3.6-35B-A3B in Focus" (a router scores 256
+ *        experts and picks 8, one shared expert sees every token; groupwise affine 4-bit
+ *        weights with a scale and a bias per 64 weights; weights rebuilt tile by tile into
+ *        bf16 for the tensor operations, fp32 accumulation) and "How It Works: Prefill and
+ *        Decode Strategies" (4-bit reconstruction inside the grouped GEMM; histogram, prefix
+ *        scan, scatter and block maps kept on the GPU with no CPU synchronisation; decode is
+ *        bandwidth-bound).
+ *   [P3] "Perplexity Open Sources Apple Chip Inference Engine Lily": the paragraph on the
+ *        target weights (MLX affine 4-bit, group size 64; the loader verifies the exact
+ *        quantisation layout and rejects other formats).
+ *
+ * The layer (fp32 output y for tokens x):
+ *   y[t] = sum_{e in topk(t)} p[t,e] * Wd_e(silu(Wg_e x[t]) * (Wu_e x[t]))
+ *        + sigmoid(wg . x[t]) * Wd_s(silu(Wg_s x[t]) * (Wu_s x[t]))
+ * with p = softmax over the selected router logits, ties in the top-k going to the lower
+ * expert index, and every W = scale * q + bias dequantised per group of 64 inputs.
+ *
+ * Conventions for every entry point:
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned, owned by the caller;
+ *     the library keeps no pointer after a call returns and allocates no device memory.
+ *     Scratch memory comes from a caller workspace sized by moe_workspace_bytes().
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls validate
+ *     their arguments on the host, then only enqueue work: no host synchronisation, no
+ *     device-to-host copy, so the sequence can be captured into a HIP graph. Results are
+ *     valid once the stream reaches that point.
+ *   - Every call returns a moe_status_t; nothing is thrown and nothing aborts. On a non-OK
+ *     return nothing was enqueued (except MOE_HIP_ERROR, which reports a failed launch).
+ *   - T = 0 returns MOE_OK and enqueues nothing.
+ *   - Calls are thread-safe provided concurrent calls use distinct workspaces and outputs.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_INVALID_ARG = 1,          /* null/misaligned pointer, negative size, bad enum      */
+  MOE_UNSUPPORTED = 2,          /* a layout the library does not implement (see below)   */
+  MOE_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below what the call needs                    */
+  MOE_HIP_ERROR = 4             /* a HIP launch failed                                   */
+} moe_status_t;
+
+/* One packed 4-bit projection family [P1 "The Model ..."], [P3 target weights]:
+ *   q     [n_mat, N, Kin/8] uint32: element 8i+j of a row at bits [4j, 4j+4) of word i
+ *   scale [n_mat, N, Kin/64] bf16, bias [n_mat, N, Kin/64] bf16
+ *   weight(m, n, k) = scale[m, n, k/64] * q(m, n, k) + bias[m, n, k/64]
+ * N is the output dimension and Kin the input dimension (rows are input-contiguous). */
+typedef struct {
+  const uint32_t* q;
+  const uint16_t* scale;
+  const uint16_t* bias;
+} moe_w4_t;
+
+/* Layer descriptor. Read during a call, never retained.
+ * Supported: bits == 4, group_size == 64, renormalize == 1, hidden and ffn multiples of 64,
+ * shared_ffn 0 (no shared expert) or a multiple of 64, 1 <= top_k <= min(num_experts, 32),
+ * num_experts <= 1024. Anything else returns MOE_UNSUPPORTED ([P3]: other layouts are
+ * rejected). */
+typedef struct {
+  int32_t hidden;        /* H  */
+  int32_t num_experts;   /* E  */
+  int32_t top_k;         /* K  */
+  int32_t ffn;           /* F  (routed expert intermediate size) */
+  int32_t shared_ffn;    /* Fs (shared expert intermediate size, 0 = none) */
+  int32_t bits;          /* must be 4  */
+  int32_t group_size;    /* must be 64 */
+  int32_t renormalize;   /* must be 1: top-k weights renormalised to sum to 1 */
+  const float* router_w;      /* [E, H] fp32 */
+  const float* router_bias;   /* [E] fp32, added to the logits before selection; or NULL */
+  moe_w4_t gate, up;          /* n_mat = E, N = F, Kin = H */
+  moe_w4_t down;              /* n_mat = E, N = H, Kin = F */
+  moe_w4_t sh_gate, sh_up;    /* n_mat = 1, N = Fs, Kin = H (ignored when Fs == 0) */
+  moe_w4_t sh_down;           /* n_mat = 1, N = H, Kin = Fs */
+  const float* shared_gate_w; /* [H] fp32: the shared expert's scale is sigmoid(wg . x) */
+} moe_layer_desc_t;
+
+/* Routing plan: device arrays written by moe_permute(), read by the grouped GEMM.
+ *   counts       [E]            tokens routed to each expert
+ *   offsets      [E+1]          exclusive prefix sum of counts (offsets[E] = T*K)
+ *   sorted_slots [T*K]          slot ids s = t*K + k grouped by expert, ascending inside a group
+ *   slot_pos     [T*K]          inverse of sorted_slots: the grouped row of slot s
+ *   blocks       [max_blocks*4] block map, one int32x4 {expert, m0, m_len, row0} per tile of
+ *                               at most MOE_BLOCK_M rows: rows m0..m0+m_len-1 of `expert`,
+ *                               which are rows row0.. of the grouped activations. Routed
+ *                               experts come first in expert order; the shared expert (id E)
+ *                               follows with its T rows (row0 = T*K + m0).
+ *   num_blocks   [1]            number of valid entries in blocks
+ * max_blocks = moe_plan_max_blocks(desc, T). */
+typedef struct {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slots;
+  int32_t* slot_pos;
+  int32_t* blocks;
+  int32_t* num_blocks;
+} moe_plan_t;
+
+#define MOE_BLOCK_M 128
+
+/* moe_grouped_gemm_w4 `which` */
+enum {
+  MOE_GEMM_GATE_UP = 0,             /* out = A [T*K*F + T*Fs] bf16: silu(G)*U per grouped row */
+  MOE_GEMM_DOWN = 1,                /* out = Y [(T*K + T), H] fp32, unweighted, grouped rows  */
+  MOE_GEMM_DOWN_COMBINE = 2,        /* out = y [T, H] fp32, the combined layer output         */
+  MOE_GEMM_DOWN_COMBINE_ATOMIC = 3  /* as 2, combined with fp32 atomics (order not fixed)     */
+};
+
+/* moe_layer_forward flags */
+enum {
+  MOE_FLAG_ATOMIC_COMBINE = 1,  /* prefill: fuse the combine into the down GEMM with atomics */
+  MOE_FLAG_FORCE_PREFILL = 2    /* use the MFMA grouped-GEMM path even for small T           */
+};
+
+/* Text for a status code (static storage; never NULL). */
+const char* moe_status_str(int status);
+
+/* Library version string, e.g. "moe_w4 1.0 gfx950". */
+const char* moe_version(void);
+
+/* Bytes of workspace that any entry point below needs for up to T_max tokens with these
+ * flags. Returns 0 if the descriptor is invalid or unsupported. */
+size_t moe_workspace_bytes(const moe_layer_desc_t* desc, int32_t T_max, int32_t flags);
+
+/* Upper bound on plan->num_blocks for T tokens: ceil(T*K/BM) + min(E, T*K) + ceil(T/BM). */
+int32_t moe_plan_max_blocks(const moe_layer_desc_t* desc, int32_t T);
+
+/* Router [P1 "The Model ..."]: for each token the top_k experts by router logit (rank order,
+ * ties to the lower expert index), their softmax-renormalised weights, the shared expert's
+ * sigmoid gate, and the per-expert token counts.
+ *   x [T, H] bf16 -> topk_idx [T, K] int32, topk_w [T, K] fp32, shared_gate [T] fp32
+ *   (may be NULL when Fs == 0), counts [E] int32.
+ * Logits are formed with fp32 accuracy (prefill: a three-part bf16 split of the fp32 router
+ * weights on bf16 MFMA; decode: fp32 FMA). workspace: moe_workspace_bytes(desc, T, 0). */
+int moe_route(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T,
+              int32_t* topk_idx, float* topk_w, float* shared_gate, int32_t* counts,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Histogram, exclusive scan, stable scatter and block map [P1 "How It Works ..."], all on
+ * the device. topk_idx [T, K] int32 with values in [0, E) (out-of-range values are counted
+ * nowhere and flagged by setting *plan->num_blocks = -1). Fills every array of `plan`.
+ * workspace: moe_workspace_bytes(desc, T, 0). */
+int moe_permute(const moe_layer_desc_t* desc, const int32_t* topk_idx, int32_t T,
+                const moe_plan_t* plan, void* workspace, size_t ws_bytes, void* stream);
+
+/* Grouped GEMM over the plan's block map with the 4-bit weights dequantised to bf16 inside
+ * the kernel and fp32 accumulation on MFMA [P1 "The Model ...", "How It Works ..."].
+ *   GATE_UP: in = x [T, H] bf16 (rows gathered through plan->sorted_slots; the shared
+ *            expert reads x in token order); out = A bf16, routed rows [T*K, F] in grouped
+ *            order followed by shared rows [T, Fs]: A = bf16(silu(x Wg^T) * (x Wu^T)).
+ *   DOWN:    in = A as above; out = Y [T*K + T, H] fp32 = A Wd^T per grouped row.
+ *   DOWN_COMBINE(_ATOMIC): in = A; out = y [T, H] fp32 =
+ *            sum_k topk_w[t,k] Y[slot_pos[t*K+k]] + shared_gate[t] * Y[T*K + t]
+ *            (overwritten, not accumulated). Needs topk_w and, when Fs > 0, shared_gate.
+ * For T <= 16 (and F, Fs <= 512, T*H <= 32768) GATE_UP and DOWN_COMBINE run the decode
+ * path's GEMV kernels (the same ones moe_layer_forward uses for such T; DOWN_COMBINE is then
+ * deterministic and needs no workspace).
+ * workspace: moe_workspace_bytes(desc, T, 0) (DOWN_COMBINE stages Y in it). */
+int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void* in, int32_t T,
+                        const moe_plan_t* plan, const float* topk_w, const float* shared_gate,
+                        void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Weighted combine: y[t] = sum_k topk_w[t,k] * y_perm[slot_pos[t*K+k]]
+ *                        + shared_gate[t] * shared_y[t]     (the shared term only if Fs > 0)
+ * y_perm [T*K, H] fp32 (grouped rows), shared_y [T, H] fp32, out [T, H] fp32 (overwritten).
+ * Deterministic: terms are added in rank order k = 0..K-1, then the shared term. */
+int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* shared_y, const float* shared_gate,
+                int32_t T, float* out, void* stream);
+
+/* The whole layer: x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path
+ * (bandwidth-bound GEMV kernels that stream only the selected experts' weights, with the
+ * combine fused into the down projection), larger T the prefill path (MFMA grouped GEMM).
+ * flags: MOE_FLAG_*. workspace: moe_workspace_bytes(desc, T, flags). */
+int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
+                      void* workspace, size_t ws_bytes, int32_t flags, void* stream);
+
+/* Test export: dequantise row `row` of matrix `mat` of a projection with input size Kin
+ * using the same device code as the GEMM kernels. out_f32 [Kin] receives scale*q + bias
+ * as computed in fp32, out_bf16 [Kin] its bf16 rounding (either may be NULL). */
+int moe_debug_dequant_w4(const moe_w4_t* w, int32_t n_rows, int32_t Kin, int32_t mat,
+                         int32_t row, float* out_f32, uint16_t* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

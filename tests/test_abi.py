@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, and
+rejects bad arguments on the host before any kernel is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_grouped_gemm_amd import moe_w4 as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_layer_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm_w4", "moe_combine", "moe_layer_forward"):
+        assert n in names
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in M.moe_version()
+    L = M.lib()
+    assert L.moe_status_str(M.MOE_OK) == b"ok"
+    assert L.moe_status_str(M.MOE_WORKSPACE_TOO_SMALL) == b"workspace too small"
+    assert L.moe_status_str(99) == b"unknown status"
+
+
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by the host checks below
+
+
+def fake_desc(H=2048, E=256, K=8, F=512, Fs=512, **over):
+    w = M.W4(FAKE, FAKE, FAKE)
+    d = M.LayerDesc(hidden=H, num_experts=E, top_k=K, ffn=F, shared_ffn=Fs, bits=4, group_size=64,
+                    renormalize=1, router_w=FAKE, router_bias=None, gate=w, up=w, down=w,
+                    sh_gate=w, sh_up=w, sh_down=w, shared_gate_w=FAKE)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def ws_bytes(d, T, flags=0):
+    return M.lib().moe_workspace_bytes(ctypes.byref(d), T, flags)
+
+
+def forward(d, T, ws, flags=0, x=FAKE, out=FAKE):
+    return M.lib().moe_layer_forward(ctypes.byref(d), x, T, out, FAKE, ws, flags, None)
+
+
+def test_workspace_sizes():
+    d = fake_desc()
+    base = ws_bytes(d, 4096)
+    atomic = ws_bytes(d, 4096, M.MOE_FLAG_ATOMIC_COMBINE)
+    # the unfused combine stages fp32 rows for T*K + T grouped rows
+    assert base - atomic >= (4096 * 8 + 4096) * 2048 * 4
+    assert ws_bytes(d, 1) < ws_bytes(d, 8) < base
+    assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 4096) == 256 + 256 + 32
+    assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 1) == 1 + 8 + 1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("bits", 3, M.MOE_UNSUPPORTED), ("group_size", 32, M.MOE_UNSUPPORTED),
+    ("renormalize", 0, M.MOE_UNSUPPORTED), ("hidden", 2000, M.MOE_UNSUPPORTED),
+    ("ffn", 500, M.MOE_UNSUPPORTED), ("shared_ffn", 100, M.MOE_UNSUPPORTED),
+    ("top_k", 300, M.MOE_UNSUPPORTED), ("num_experts", 2048, M.MOE_UNSUPPORTED),
+    ("top_k", 0, M.MOE_INVALID_ARG), ("hidden", -64, M.MOE_INVALID_ARG),
+    ("router_w", None, M.MOE_INVALID_ARG), ("router_w", FAKE + 4, M.MOE_INVALID_ARG),
+    ("shared_gate_w", None, M.MOE_INVALID_ARG),
+])
+def test_descriptor_rejections(field, value, status):
+    d = fake_desc(**{field: value})
+    assert forward(d, 4, 1 << 40) == status
+    assert ws_bytes(d, 4) == 0
+
+
+def test_weight_pointer_rejections():
+    d = fake_desc()
+    d.down = M.W4(FAKE + 8, FAKE, FAKE)          # q must be 16-byte aligned
+    assert forward(d, 4, 1 << 40) == M.MOE_INVALID_ARG
+    d = fake_desc()
+    d.sh_up = M.W4(None, FAKE, FAKE)
+    assert forward(d, 4, 1 << 40) == M.MOE_INVALID_ARG
+    d = fake_desc(shared_ffn=0, shared_gate_w=None)   # no shared expert: its pointers unused
+    d.sh_up = M.W4(None, None, None)
+    assert forward(d, 0, 0) == M.MOE_OK
+
+
+def test_call_rejections_before_launch():
+    d = fake_desc()
+    need = ws_bytes(d, 64)
+    assert forward(d, 64, need - 1) == M.MOE_WORKSPACE_TOO_SMALL
+    assert forward(d, -1, need) == M.MOE_INVALID_ARG
+    assert forward(d, 0, 0) == M.MOE_OK                     # T = 0 is a no-op
+    assert forward(d, 64, need, flags=8) == M.MOE_INVALID_ARG
+    assert forward(d, 64, need, x=FAKE + 2) == M.MOE_INVALID_ARG
+    assert forward(d, 64, need, out=None) == M.MOE_INVALID_ARG
+    L = M.lib()
+    assert L.moe_route(ctypes.byref(d), FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) \
+        == M.MOE_INVALID_ARG                                   # shared_gate needed when Fs > 0
+    assert L.moe_route(ctypes.byref(d), FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) \
+        == M.MOE_WORKSPACE_TOO_SMALL
+    plan = M.Plan(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE)      # blocks must be 16-byte aligned
+    assert L.moe_permute(ctypes.byref(d), FAKE, 4, ctypes.byref(plan), FAKE, 1 << 30, None) \
+        == M.MOE_INVALID_ARG
+    plan = M.Plan(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_grouped_gemm_w4(ctypes.byref(d), 7, FAKE, 4, ctypes.byref(plan), None, None,
+                                 FAKE, FAKE, 1 << 30, None) == M.MOE_INVALID_ARG
+    assert L.moe_grouped_gemm_w4(ctypes.byref(d), M.MOE_GEMM_DOWN_COMBINE, FAKE, 4,
+                                 ctypes.byref(plan), None, FAKE, FAKE, FAKE, 1 << 30, None) \
+        == M.MOE_INVALID_ARG                                   # combine needs topk_w
+    assert L.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 4, FAKE, None) \
+        == M.MOE_INVALID_ARG                                   # shared_y needed when Fs > 0
+    w = M.W4(FAKE, FAKE, FAKE)
+    assert L.moe_debug_dequant_w4(ctypes.byref(w), 4, 128, 0, 4, FAKE, None, None) \
+        == M.MOE_INVALID_ARG                                   # row out of range
+    assert L.moe_debug_dequant_w4(ctypes.byref(w), 4, 96, 0, 0, FAKE, None, None) \
+        == M.MOE_UNSUPPORTED
