@@ -63,7 +63,7 @@ bool sizes_ok(const Dims& d) {
 
 // Workspace regions for T tokens, in order of use.
 struct Layout {
-  size_t logits, rsplit, hist, topk_idx, topk_w, sgate;
+  size_t logits, hist, topk_idx, topk_w, sgate;
   size_t counts, offsets, sorted, slotpos, blocks, nblk;
   size_t a, y;
   size_t end_route, end_permute, end_no_y, total;
@@ -75,7 +75,6 @@ Layout layout_of(const Dims& d, int flags) {
   const size_t TK = (size_t)d.T * d.K;
   const int nchunks = (int)((TK + kChunkSlots - 1) / kChunkSlots);
   L.logits = o;  o = align_up(o + (size_t)d.T * d.E * 4);
-  L.rsplit = o;  o = align_up(o + (size_t)3 * d.E * d.H * 2);
   L.end_route = o;
   L.hist = o;    o = align_up(o + (size_t)nchunks * (d.E + 1) * 4);
   L.end_permute = o;
@@ -115,10 +114,7 @@ int run_route(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, in
   if (decode) {
     e = launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
   } else {
-    uint16_t* parts = at<uint16_t>(ws, L.rsplit);
-    e = launch_router_split(desc->router_w, d.E, d.H, parts, s);
-    if (e != hipSuccess) return MOE_HIP_ERROR;
-    e = launch_router_logits_mfma(x, parts, desc->router_bias, d.T, d.E, d.H, logits, s);
+    e = launch_router_logits_mfma(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
   }
   if (e != hipSuccess) return MOE_HIP_ERROR;
   const float* wg = d.Fs > 0 ? desc->shared_gate_w : nullptr;
@@ -314,14 +310,22 @@ int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T
   uint16_t* a = at<uint16_t>(workspace, L.a);
   const int mb = max_blocks(d);
 
+  if (decode) {
+    // router GEMV, then top-k + permutation + block map in one workgroup, then the two GEMVs
+    float* logits = at<float>(workspace, L.logits);
+    if (launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits,
+                                  s) != hipSuccess)
+      return MOE_HIP_ERROR;
+    if (launch_route_small(logits, x, d.Fs > 0 ? desc->shared_gate_w : nullptr, d, idx, w, sgate,
+                           plan, s) != hipSuccess)
+      return MOE_HIP_ERROR;
+    if (launch_dec_gateup(d, *desc, x, plan, mb, a, s) != hipSuccess) return MOE_HIP_ERROR;
+    return hip_status(launch_dec_down(d, *desc, a, plan, w, sgate, out, s));
+  }
   st = run_route(desc, d, x, idx, w, sgate, workspace, L, decode, s);
   if (st != MOE_OK) return st;
   if (launch_permute(idx, d, d.Fs > 0, at<int32_t>(workspace, L.hist), plan, s) != hipSuccess)
     return MOE_HIP_ERROR;
-  if (decode) {
-    if (launch_dec_gateup(d, *desc, x, plan, mb, a, s) != hipSuccess) return MOE_HIP_ERROR;
-    return hip_status(launch_dec_down(d, *desc, a, plan, w, sgate, out, s));
-  }
   const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);
   if (launch_gemm_w4(kGateUp, pg, mb, s) != hipSuccess) return MOE_HIP_ERROR;
   if (flags & MOE_FLAG_ATOMIC_COMBINE) {

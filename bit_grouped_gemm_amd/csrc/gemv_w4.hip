@@ -33,15 +33,6 @@ __global__ __launch_bounds__(256) void k_dec_gateup(
   const int f_base = blockIdx.x * 16;
   if (f_base >= Ne) return;  // uniform, before the barrier
 
-  // stage the block's token rows
-  const int h8 = H >> 3;
-  for (int v = threadIdx.x; v < m_len * h8; v += 256) {
-    const int i = v / h8, c = v - i * h8;
-    const int tok = shared ? (m0 + i) : (sorted_slots[row0 + i] / K);
-    reinterpret_cast<uint4*>(xs)[v] = reinterpret_cast<const uint4*>(x + (size_t)tok * H)[c];
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t* gq = shared ? sh_gate.q : gate.q + (size_t)e * F * (H >> 3);
   const uint32_t* uq = shared ? sh_up.q : up.q + (size_t)e * F * (H >> 3);
@@ -50,16 +41,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(
   const uint16_t* us = shared ? sh_up.scale : up.scale + (size_t)e * F * (H >> 6);
   const uint16_t* ub = shared ? sh_up.bias : up.bias + (size_t)e * F * (H >> 6);
 
-  float pg[4][TC], pu[4][TC];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int i = 0; i < TC; ++i) pg[r][i] = pu[r][i] = 0.0f;
-
   const int U = H >> 5;  // 32-input units per row (one 16-byte load)
-  for (int u = lane; u < U; u += 64) {
-    uint4 wgq[4], wuq[4];
-    float sg[4], bg[4], su[4], bu[4];
+  uint4 wgq[4], wuq[4];
+  float sg[4], bg[4], su[4], bu[4];
+  auto load_w = [&](int u) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int f = min(f_base + wave * 4 + r, Ne - 1);
@@ -71,6 +56,26 @@ __global__ __launch_bounds__(256) void k_dec_gateup(
       su[r] = bf16_to_f32(us[g]);
       bu[r] = bf16_to_f32(ub[g]);
     }
+  };
+  if (lane < U) load_w(lane);  // in flight while the token rows are staged
+
+  // stage the block's token rows
+  const int h8 = H >> 3;
+  for (int v = threadIdx.x; v < m_len * h8; v += 256) {
+    const int i = v / h8, c = v - i * h8;
+    const int tok = shared ? (m0 + i) : (sorted_slots[row0 + i] / K);
+    reinterpret_cast<uint4*>(xs)[v] = reinterpret_cast<const uint4*>(x + (size_t)tok * H)[c];
+  }
+  __syncthreads();
+
+  float pg[4][TC], pu[4][TC];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < TC; ++i) pg[r][i] = pu[r][i] = 0.0f;
+
+  for (int u = lane; u < U; u += 64) {
+    if (u != lane) load_w(u);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint32_t wg[16], wu[16];
@@ -155,21 +160,26 @@ hipError_t launch_dec_gateup(const Dims& d, const moe_layer_desc_t& desc, const 
 // with each of the block's activation rows and adds it, times the token's routing weight (or
 // the shared gate), into that token's accumulator. Lane (l & 15) = t holds token t's sum, so
 // the order of additions is fixed: the result is deterministic.
-template <int TC>
+// The weights of up to kNB blocks (4 for T > 4) are requested before any arithmetic; when the activations
+// of the whole call are small (T <= 4 at F = 512) they are staged once into LDS alongside.
+constexpr int kNB = 16;
+constexpr int kDownLdsBytes = 40 * 1024;
+
+template <int TC, bool kLds>
 __global__ __launch_bounds__(256) void k_dec_down(
     const int4* __restrict__ blocks, const int* __restrict__ num_blocks,
     const int32_t* __restrict__ sorted_slots, const uint16_t* __restrict__ a, int H, int E, int K,
     int F, int Fs, int TK, moe_w4_t down, moe_w4_t sh_down, const float* __restrict__ topk_w,
     const float* __restrict__ sgate, int T, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t as[];  // A rows (kLds only)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, sl = lane & 15;
   const int h = blockIdx.x * 16 + wave * 4 + grp;
-  const bool hvalid = h < H;
-  const int hh = hvalid ? h : 0;
+  const int hh = h < H ? h : H - 1;
   const int nblk = *num_blocks;
   float acc = 0.0f;  // token sl's running sum for row h
 
-  constexpr int NB = 8;  // blocks whose weights are in flight together
+  constexpr int NB = TC <= 4 ? kNB : 4;
   for (int jb = 0; jb < nblk; jb += NB) {
     int4 blk[NB];
     uint4 wq[NB];
@@ -191,10 +201,17 @@ __global__ __launch_bounds__(256) void k_dec_down(
         wb[b] = bf16_to_f32(bp[(size_t)hh * (Kd >> 6) + (sl >> 1)]);
       }
     }
+    if (kLds && jb == 0) {  // all activation rows of the call: [TK][F] then [T][Fs]
+      const int n16 = (TK * F + T * Fs) >> 3;
+      for (int v = threadIdx.x; v < n16; v += 256)
+        reinterpret_cast<uint4*>(as)[v] = reinterpret_cast<const uint4*>(a)[v];
+      __syncthreads();
+    }
+    const uint16_t* abase = kLds ? as : a;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int e = blk[b].x;
-      if (e < 0) break;  // uniform: trailing entries of the last batch
+      if (e < 0) continue;  // uniform: trailing entries of the last batch
       const bool sh = e >= E;
       const int Kd = sh ? Fs : F;
       const int m0 = blk[b].y, m_len = blk[b].z, row0 = blk[b].w;
@@ -209,8 +226,8 @@ __global__ __launch_bounds__(256) void k_dec_down(
         if (i < m_len) {
           float part = 0.0f;
           if (lane_has) {
-            const uint16_t* ar = sh ? a + (size_t)TK * F + (size_t)(m0 + i) * Fs
-                                    : a + (size_t)(row0 + i) * F;
+            const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)(m0 + i) * Fs
+                                    : abase + (size_t)(row0 + i) * F;
             const uint4* av = reinterpret_cast<const uint4*>(ar + sl * 32);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(256) void k_dec_down(
       }
     }
   }
-  if (hvalid && sl < T) out[(size_t)sl * H + h] = acc;
+  if (h < H && sl < T) out[(size_t)sl * H + h] = acc;
 }
 
 hipError_t launch_dec_down(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* a,
@@ -246,20 +263,23 @@ hipError_t launch_dec_down(const Dims& d, const moe_layer_desc_t& desc, const ui
                            float* out, hipStream_t s) {
   dim3 grid((d.H + 15) / 16);
   const int4* blocks = reinterpret_cast<const int4*>(plan.blocks);
-#define MOE_DEC_DN(TCV)                                                                    \
-  hipLaunchKernelGGL(k_dec_down<TCV>, grid, dim3(256), 0, s, blocks, plan.num_blocks,       \
-                     plan.sorted_slots, a, d.H, d.E, d.K, d.F, d.Fs, d.TK(), desc.down,        \
-                     desc.sh_down, topk_w, sgate, d.T, out)
-  if (d.T <= 1)
-    MOE_DEC_DN(1);
-  else if (d.T <= 2)
-    MOE_DEC_DN(2);
-  else if (d.T <= 4)
-    MOE_DEC_DN(4);
-  else if (d.T <= 8)
-    MOE_DEC_DN(8);
-  else
-    MOE_DEC_DN(16);
+  const size_t abytes = ((size_t)d.TK() * d.F + (size_t)d.T * d.Fs) * sizeof(uint16_t);
+  const bool lds = abytes <= (size_t)kDownLdsBytes;
+#define MOE_DEC_DN(TCV, L)                                                                    \
+  hipLaunchKernelGGL((k_dec_down<TCV, L>), grid, dim3(256), L ? abytes : 0, s, blocks,         \
+                     plan.num_blocks, plan.sorted_slots, a, d.H, d.E, d.K, d.F, d.Fs, d.TK(),   \
+                     desc.down, desc.sh_down, topk_w, sgate, d.T, out)
+  if (d.T <= 1) {
+    if (lds) MOE_DEC_DN(1, true); else MOE_DEC_DN(1, false);
+  } else if (d.T <= 2) {
+    if (lds) MOE_DEC_DN(2, true); else MOE_DEC_DN(2, false);
+  } else if (d.T <= 4) {
+    if (lds) MOE_DEC_DN(4, true); else MOE_DEC_DN(4, false);
+  } else if (d.T <= 8) {
+    MOE_DEC_DN(8, false);
+  } else {
+    MOE_DEC_DN(16, false);
+  }
 #undef MOE_DEC_DN
   return hipGetLastError();
 }

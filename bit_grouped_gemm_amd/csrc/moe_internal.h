@@ -40,14 +40,16 @@ struct GemmParams {
 enum GemmMode { kGateUp = 0, kDownStore = 1, kDownAtomic = 2 };
 
 // Launchers (return the launch status).
-hipError_t launch_router_split(const float* w, int E, int H, uint16_t* parts, hipStream_t s);
-hipError_t launch_router_logits_mfma(const uint16_t* x, const uint16_t* parts, const float* bias,
-                                     int T, int E, int H, float* logits, hipStream_t s);
+hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias, int T,
+                                     int E, int H, float* logits, hipStream_t s);
 hipError_t launch_router_logits_gemv(const uint16_t* x, const float* w, const float* bias, int T,
                                      int E, int H, float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, const uint16_t* x, const float* wg, int T, int E,
                        int K, int H, int32_t* idx, float* w, float* sgate, hipStream_t s);
 hipError_t launch_count(const int32_t* idx, int TK, int E, int32_t* counts, hipStream_t s);
+hipError_t launch_route_small(const float* logits, const uint16_t* x, const float* wg,
+                              const Dims& d, int32_t* idx, float* w, float* sgate,
+                              const moe_plan_t& plan, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_t* hist,
                           const moe_plan_t& plan, hipStream_t s);
 hipError_t launch_gemm_w4(int mode, const GemmParams& p, int max_blocks, hipStream_t s);
@@ -140,6 +142,82 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Top-k of one token's E logits by one wave (E <= 64*NJ): lane l holds logits e = l + 64*j.
+// K rounds of a wave arg-max ordered by (larger logit, then lower expert index); lane r ends
+// with the rank-r winner (my_v, my_i), lanes >= K with -inf.
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lt, int E, int K, int lane,
+                                          float& my_v, int& my_i) {
+  float v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? lt[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  my_v = -INFINITY;
+  my_i = 0;
+  for (int r = 0; r < K; ++r) {
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u) && (v[j] > best || (v[j] == best && e < bi))) {
+        best = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > best || (ov == best && oi < bi)) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) {
+      my_v = best;
+      my_i = bi;
+    }
+  }
+}
+
+// x . wg for one token (bf16 x, fp32 wg), by one wave: lane l takes the contiguous inputs
+// [l*H/64, (l+1)*H/64) in pieces of four, all loads issued before the FMAs. H % 64 == 0.
+__device__ __forceinline__ float shared_gate_logit(const uint16_t* __restrict__ xt,
+                                                   const float* __restrict__ wg, int H, int lane) {
+  const int per = H >> 6;  // inputs per lane
+  const int base = lane * per;
+  float g0 = 0.0f, g1 = 0.0f;
+  int i = 0;
+  for (; i + 32 <= per; i += 32) {  // 64 B of x and 128 B of wg per step
+    uint4 xv[4];
+    float4 wv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = *reinterpret_cast<const uint4*>(xt + base + i + 8 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = *reinterpret_cast<const float4*>(wg + base + i + 4 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xw[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+      const float4 a = wv[2 * j], b = wv[2 * j + 1];
+      g0 = __builtin_fmaf(bf16_to_f32(xw[0] & 0xFFFFu), a.x, g0);
+      g1 = __builtin_fmaf(bf16_to_f32(xw[0] >> 16), a.y, g1);
+      g0 = __builtin_fmaf(bf16_to_f32(xw[1] & 0xFFFFu), a.z, g0);
+      g1 = __builtin_fmaf(bf16_to_f32(xw[1] >> 16), a.w, g1);
+      g0 = __builtin_fmaf(bf16_to_f32(xw[2] & 0xFFFFu), b.x, g0);
+      g1 = __builtin_fmaf(bf16_to_f32(xw[2] >> 16), b.y, g1);
+      g0 = __builtin_fmaf(bf16_to_f32(xw[3] & 0xFFFFu), b.z, g0);
+      g1 = __builtin_fmaf(bf16_to_f32(xw[3] >> 16), b.w, g1);
+    }
+  }
+  for (; i < per; ++i) g0 = __builtin_fmaf(bf16_to_f32(xt[base + i]), wg[base + i], g0);
+  return wave_sum(g0 + g1);
 }
 #endif  // __HIPCC__
 

@@ -140,6 +140,88 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ idx,
   }
 }
 
+// Decode routing in one workgroup (T <= 16 tokens, E <= 1024): wave t selects token t's top-k
+// (softmax-renormalised) and its shared gate, then the workgroup builds counts, offsets,
+// the block map (one block per active expert: an expert holds at most T < 128 rows) and the
+// stable permutation. Inside an expert, slot (t, k) has rank #{t' < t routed to it}, read off
+// a per-expert token bitmask.
+template <int NJ>
+__global__ __launch_bounds__(1024) void k_route_small(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, const float* __restrict__ wg,
+    int T, int E, int K, int H, int32_t* __restrict__ idx, float* __restrict__ wout,
+    float* __restrict__ sgate, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_pos, int4* __restrict__ blocks,
+    int32_t* __restrict__ num_blocks) {
+  __shared__ int cnt[1024];
+  __shared__ unsigned mask[1024];
+  __shared__ int off_s[1024];
+  __shared__ int wave_tot[16];
+  __shared__ int total_slots, total_blocks;
+  const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
+  cnt[tid] = 0;
+  mask[tid] = 0u;
+  __syncthreads();
+  float my_v = -INFINITY;
+  int my_i = 0;
+  if (t < T) {
+    wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i);
+    const float vmax = __shfl(my_v, 0, 64);
+    const float z = lane < K ? __expf(my_v - vmax) : 0.0f;
+    const float den = wave_sum(z);
+    if (lane < K) {
+      idx[t * K + lane] = my_i;
+      wout[t * K + lane] = z / den;
+      atomicAdd(&cnt[my_i], 1);
+      atomicOr(&mask[my_i], 1u << t);
+    }
+    if (wg != nullptr) {
+      const float g = shared_gate_logit(x + (size_t)t * H, wg, H, lane);
+      if (lane == 0) sgate[t] = 1.0f / (1.0f + __expf(-g));
+    }
+  }
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int off = block_exclusive_scan_1024(c, wave_tot, &total_slots);
+  const int bo = block_exclusive_scan_1024(c > 0 ? 1 : 0, wave_tot, &total_blocks);
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = off;
+    off_s[tid] = off;
+    if (c > 0) blocks[bo] = make_int4(tid, 0, c, off);
+  }
+  if (tid == 0) {
+    offsets[E] = total_slots;
+    int nb = total_blocks;
+    if (wg != nullptr) blocks[nb++] = make_int4(E, 0, T, T * K);
+    *num_blocks = nb;
+  }
+  __syncthreads();
+  if (t < T && lane < K) {
+    const int pos = off_s[my_i] + __popc(mask[my_i] & ((1u << t) - 1u));
+    sorted_slots[pos] = t * K + lane;
+    slot_pos[t * K + lane] = pos;
+  }
+}
+
+hipError_t launch_route_small(const float* logits, const uint16_t* x, const float* wg,
+                              const Dims& d, int32_t* idx, float* w, float* sgate,
+                              const moe_plan_t& plan, hipStream_t s) {
+#define MOE_RS(NJ)                                                                           \
+  hipLaunchKernelGGL(k_route_small<NJ>, dim3(1), dim3(1024), 0, s, logits, x, wg, d.T, d.E, d.K, \
+                     d.H, idx, w, sgate, plan.counts, plan.offsets, plan.sorted_slots,            \
+                     plan.slot_pos, reinterpret_cast<int4*>(plan.blocks), plan.num_blocks)
+  if (d.E <= 64)
+    MOE_RS(1);
+  else if (d.E <= 256)
+    MOE_RS(4);
+  else if (d.E <= 512)
+    MOE_RS(8);
+  else
+    MOE_RS(16);
+#undef MOE_RS
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_t* hist,
                           const moe_plan_t& plan, hipStream_t s) {
   const int TK = d.TK();
