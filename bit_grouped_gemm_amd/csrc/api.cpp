@@ -63,7 +63,7 @@ bool sizes_ok(const Dims& d) {
 
 // Workspace regions for T tokens, in order of use.
 struct Layout {
-  size_t logits, hist, topk_idx, topk_w, sgate;
+  size_t logits, hist, topk_idx, topk_w, sgate, droute;
   size_t counts, offsets, sorted, slotpos, blocks, nblk;
   size_t a, y;
   size_t end_route, end_permute, end_no_y, total;
@@ -74,13 +74,14 @@ Layout layout_of(const Dims& d, int flags) {
   size_t o = 0;
   const size_t TK = (size_t)d.T * d.K;
   const int nchunks = (int)((TK + kChunkSlots - 1) / kChunkSlots);
-  L.logits = o;  o = align_up(o + (size_t)d.T * d.E * 4);
+  L.logits = o;  o = align_up(o + (size_t)d.T * (d.E + 1) * 4);
   L.end_route = o;
   L.hist = o;    o = align_up(o + (size_t)nchunks * (d.E + 1) * 4);
   L.end_permute = o;
   L.topk_idx = o; o = align_up(o + TK * 4);
   L.topk_w = o;  o = align_up(o + TK * 4);
   L.sgate = o;   o = align_up(o + (size_t)d.T * 4);
+  L.droute = o;  o = align_up(o + decode_route_bytes(d));
   L.counts = o;  o = align_up(o + (size_t)d.E * 4);
   L.offsets = o; o = align_up(o + (size_t)(d.E + 1) * 4);
   L.sorted = o;  o = align_up(o + TK * 4);
@@ -295,7 +296,8 @@ int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T
   if (T == 0) return MOE_OK;
   const Dims d = dims_of(desc, T);
   if (!sizes_ok(d)) return MOE_UNSUPPORTED;
-  if (!x || !aligned(x, 16) || !out || !aligned(out, 16) || !workspace) return MOE_INVALID_ARG;
+  if (!x || !aligned(x, 16) || !out || !aligned(out, 16) || !workspace || !aligned(workspace, 256))
+    return MOE_INVALID_ARG;
   const Layout L = layout_of(d, flags);
   if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -310,6 +312,11 @@ int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T
   uint16_t* a = at<uint16_t>(workspace, L.a);
   const int mb = max_blocks(d);
 
+  if (decode && decode_fast_ok(d)) {
+    // three launches: router + shared expert, top-k + routed gate/up, down + combine
+    const DecodeBufs b{at<float>(workspace, L.logits), at<int32_t>(workspace, L.droute), a};
+    return hip_status(launch_decode_layer(d, *desc, x, b, out, s));
+  }
   if (decode) {
     // router GEMV, then top-k + permutation + block map in one workgroup, then the two GEMVs
     float* logits = at<float>(workspace, L.logits);

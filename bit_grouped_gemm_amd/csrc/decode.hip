@@ -1,0 +1,586 @@
+// Decode path of moe_layer_forward (T <= 16 tokens): the whole MoE layer in three launches.
+//
+// "Perplexity's Lily: A Breakthrough Local Inference Engine Tailored Exclusively for Apple
+// Silicon", section "How It Works: Prefill and Decode Strategies": batch-1 decode barely reuses
+// weights, so it is bound by the bytes moved per token, and a decode step made of many small
+// dependent kernels is dominated by their sequencing; routing stays on the GPU with no CPU
+// synchronisation. Section "The Model: Qwen3.6-35B-A3B in Focus": a router scores the experts
+// and picks eight, one shared expert sees every token, and the 4-bit group-64 weights are
+// rebuilt into bf16 for the tensor operations with fp32 accumulation.
+//
+// The layer has two all-to-all dependencies (every routed expert needs all router logits;
+// every output row needs the complete SwiGLU activation of each selected expert), so it is cut
+// into exactly three kernels; on gfx950 a kernel boundary inside a HIP graph costs less than a
+// software grid barrier with the agent-scope fences that cross-XCD visibility needs.
+//   A (k_dec_a): the routing-independent work: router logits (one wave per expert row, fp32 FMA
+//     on the fp32 weights), the shared expert's gate logit, and the shared expert's gate/up rows
+//     with SwiGLU (one wave per row pair);
+//   B (k_dec_b): every workgroup selects each token's top-k from the logits (the same result in
+//     all of them), groups the (token, rank) slots by expert in LDS (stable grouped rows by
+//     counting), and its waves stream the selected experts' gate/up rows (a 1 KiB row per wave,
+//     16 bytes per lane), dequantise them in registers and store A = bf16(silu(G) * U);
+//     workgroup 0 also stores the per-expert route record for C;
+//   C (k_dec_c): down projection fused with the weighted combine. The route record and the
+//     activations are staged in LDS; a 32-lane half wave owns output row h, its two 16-lane
+//     groups walk the even and odd entries of the expert list (ascending expert id, then the
+//     shared expert) and add their two partial sums in a fixed order, so the result is
+//     deterministic.
+// Every selected weight byte is read from HBM once per call.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+constexpr int kCH = 4;  // 16-byte chunks (32 inputs) per lane of a gate/up row (H <= 2048)
+constexpr int kNB = 8;  // down rows requested per batch by one 16-lane group
+}  // namespace
+
+struct DecodeArgs {
+  const uint16_t* x;
+  const float* router_w;
+  const float* router_bias;
+  const float* wg;  // shared-gate weights, or null when there is no shared expert
+  moe_w4_t gate, up, down, sh_gate, sh_up, sh_down;
+  int T, H, E, K, F, Fs;
+  DecodeBufs b;
+  float* out;       // [T, H]
+};
+
+// Butterfly sum of v[0..N) over aligned groups of W lanes (W = 16 or 64, N a power of two).
+// Afterwards lane r of a group (r = lane % W) holds in v[0 .. N/W) the totals of entries
+// (N/W)*r ... when N >= W, and otherwise in v[0] the total of entry r*N/W. Steps inside a row
+// of 16 lanes use DPP; the steps across rows (distance 16, 32) use ds_bpermute.
+template <int N, int W, int O>
+__device__ __forceinline__ void group_reduce_step(float (&v)[N], int r) {
+  if constexpr (O >= 1) {
+    constexpr int live = (N * 2 * O / W) > 1 ? (N * 2 * O / W) : 1;
+    if constexpr (live >= 2) {
+      constexpr int h = live / 2;
+      const bool up = (r & O) != 0;
+#pragma unroll
+      for (int j = 0; j < h; ++j) {
+        const float keep = up ? v[j + h] : v[j];
+        const float send = up ? v[j] : v[j + h];
+        v[j] = keep + (O <= 8 ? dpp_partner16<O>(send) : __shfl_xor(send, O, 64));
+      }
+    } else {
+      v[0] += O <= 8 ? dpp_partner16<O>(v[0]) : __shfl_xor(v[0], O, 64);
+    }
+    group_reduce_step<N, W, O / 2>(v, r);
+  }
+}
+
+template <int N, int W>
+__device__ __forceinline__ void group_reduce(float (&v)[N], int r) {
+  group_reduce_step<N, W, W / 2>(v, r);
+}
+
+// One lane's share of a gate row and an up row: the 32-input chunk c = lane (H <= 2048: one
+// 16-byte load per row and lane, a 1 KiB row per wave).
+struct PairW {
+  uint4 g, u;
+  float gs, gb, us, ub;
+};
+
+__device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe_w4_t& U,
+                                          size_t row, int H, int lane) {
+  if (lane < (H >> 5)) {
+    const size_t sidx = row * (size_t)(H >> 6) + (lane >> 1);
+    w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[lane];
+    w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[lane];
+    w.gs = bf16_to_f32(G.scale[sidx]);
+    w.gb = bf16_to_f32(G.bias[sidx]);
+    w.us = bf16_to_f32(U.scale[sidx]);
+    w.ub = bf16_to_f32(U.bias[sidx]);
+  } else {
+    w.g = w.u = make_uint4(0, 0, 0, 0);
+    w.gs = w.gb = w.us = w.ub = 0.0f;
+  }
+}
+
+// Partial gate and up dot products of the lane's chunk with the m tokens listed in tok (token
+// ids into the LDS copy of x; null = tokens 0..m-1). The chunk is dequantised once and used for
+// all tokens. v[2j], v[2j+1] = gate, up partial of entry j.
+template <int TC>
+__device__ __forceinline__ void pair_dots(const PairW& w, const uint16_t* xs, int H, int lane,
+                                          const int* tok, int m, float (&v)[2 * TC]) {
+#pragma unroll
+  for (int j = 0; j < 2 * TC; ++j) v[j] = 0.0f;
+  if (lane >= (H >> 5)) return;
+  uint32_t dg[16], du[16];
+  dequant8(w.g.x, w.gs, w.gb, dg + 0);
+  dequant8(w.g.y, w.gs, w.gb, dg + 4);
+  dequant8(w.g.z, w.gs, w.gb, dg + 8);
+  dequant8(w.g.w, w.gs, w.gb, dg + 12);
+  dequant8(w.u.x, w.us, w.ub, du + 0);
+  dequant8(w.u.y, w.us, w.ub, du + 4);
+  dequant8(w.u.z, w.us, w.ub, du + 8);
+  dequant8(w.u.w, w.us, w.ub, du + 12);
+#pragma unroll
+  for (int j = 0; j < TC; ++j) {
+    if (j < m) {
+      const int t = tok ? tok[j] : j;
+      const uint4* xr = reinterpret_cast<const uint4*>(xs + (size_t)t * H + 32 * lane);
+      float ag = 0.0f, au = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 xv = xr[q];
+        ag = dot2_bf16(xv.x, dg[4 * q + 0], ag);
+        ag = dot2_bf16(xv.y, dg[4 * q + 1], ag);
+        ag = dot2_bf16(xv.z, dg[4 * q + 2], ag);
+        ag = dot2_bf16(xv.w, dg[4 * q + 3], ag);
+        au = dot2_bf16(xv.x, du[4 * q + 0], au);
+        au = dot2_bf16(xv.y, du[4 * q + 1], au);
+        au = dot2_bf16(xv.z, du[4 * q + 2], au);
+        au = dot2_bf16(xv.w, du[4 * q + 3], au);
+      }
+      v[2 * j] = ag;
+      v[2 * j + 1] = au;
+    }
+  }
+}
+
+// Reduce the gate/up partials over the wave and store A = bf16(silu(g) * u) of entry j at
+// a[a_row(j) + f]. After the reduction lane r holds entry r*2TC/64; u_j sits 32/TC lanes above
+// g_j.
+template <int TC, typename RowFn>
+__device__ __forceinline__ void pair_finish(float (&v)[2 * TC], int lane, int m, int f,
+                                            uint16_t* a, RowFn a_row) {
+  group_reduce<2 * TC, 64>(v, lane);
+  constexpr int s = 32 / TC;
+  const float u = __shfl_xor(v[0], s, 64);
+  const int j = lane / (2 * s);
+  if (lane % (2 * s) == 0 && j < m) a[a_row(j) + f] = f32_to_bf16(silu_mul(v[0], u));
+}
+
+// Routing of one call as per-expert entries, in LDS. Entry d (d < D, ascending expert id) is
+// expert ent_e[d] with ent_m[d] tokens, whose grouped rows start at ent_row0[d]; bit t of
+// ent_mask[d] is set if token t routes to it. Grouped row r belongs to token row_tok[r] with
+// routing weight row_w[r] (tokens ascending inside an expert). The words from `nd` through sgs
+// are also the route record that B hands to C.
+struct Route {
+  int* nd;            // [1] D
+  int* ent_e;         // [TK]
+  int* ent_m;         // [TK]
+  int* ent_row0;      // [TK]
+  unsigned* ent_mask; // [TK]
+  float* row_w;       // [TK]
+  float* sgs;         // [T] shared-expert gate
+  int* row_tok;       // [TK] (B only)
+};
+
+__host__ __device__ __forceinline__ size_t route_words(int TK, int T) { return 1 + 5 * (size_t)TK + T; }
+
+__device__ __forceinline__ Route carve_route(void* base, int TK, int T) {
+  Route R;
+  R.nd = reinterpret_cast<int*>(base);
+  R.ent_e = R.nd + 1;
+  R.ent_m = R.ent_e + TK;
+  R.ent_row0 = R.ent_m + TK;
+  R.ent_mask = reinterpret_cast<unsigned*>(R.ent_row0 + TK);
+  R.row_w = reinterpret_cast<float*>(R.ent_mask + TK);
+  R.sgs = R.row_w + TK;
+  R.row_tok = reinterpret_cast<int*>(R.sgs + T);
+  return R;
+}
+
+// Entries from the slots' experts sel_idx[TK] and weights sel_w[TK] (slot s = t*K + k); cnt and
+// tmask [E] were filled while the top-k was written (each token routes to an expert at most
+// once). Wave 0 scans the counts with DPP (E/64 consecutive experts per lane) and writes the
+// entries in ascending expert order and each expert's first grouped row into off[E]; then slot
+// s goes to grouped row off[e] + #{tokens t' < t routed to e} (stable). Ends with a barrier.
+__device__ void build_route(const Route& R, const int* sel_idx, const float* sel_w,
+                            const int* cnt, const unsigned* tmask, int* off, int T, int E, int K) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int per = (E + 63) >> 6;  // experts per lane (<= 16)
+    const int e0 = tid * per;
+    int rows = 0, nz = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      const int c = e < E ? cnt[e] : 0;
+      rows += c;
+      nz += c > 0;
+    }
+    const int packed = (rows << 16) | nz;  // grouped rows < 2^15
+    const int incl = wave_incl_scan(packed, tid);
+    int row = (incl - packed) >> 16, d = (incl - packed) & 0xFFFF;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        const int c = cnt[e];
+        off[e] = row;
+        if (c > 0) {
+          R.ent_e[d] = e;
+          R.ent_m[d] = c;
+          R.ent_row0[d] = row;
+          R.ent_mask[d] = tmask[e];
+          ++d;
+        }
+        row += c;
+      }
+    }
+    if (tid == 63) *R.nd = incl & 0xFFFF;
+  }
+  __syncthreads();
+  const int TK = T * K;
+  for (int s = tid; s < TK; s += blockDim.x) {
+    const int e = sel_idx[s], t = s / K;
+    const int r = off[e] + __popc(tmask[e] & ((1u << t) - 1u));
+    R.row_tok[r] = t;
+    R.row_w[r] = sel_w[s];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void stage_x(uint16_t* xs, const uint16_t* __restrict__ x, int n8) {
+  for (int v = threadIdx.x; v < n8; v += 256)
+    reinterpret_cast<uint4*>(xs)[v] = reinterpret_cast<const uint4*>(x)[v];
+}
+
+// ============================================================================ A
+// Tasks (one per wave): [0, E) router rows, E: shared-gate logit, then one task per row f of the
+// shared expert's gate and up matrices.
+template <int TC>
+__global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint4 smem[];
+  const int T = p.T, H = p.H, E = p.E, F = p.F, Fs = p.Fs, TK = T * p.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int task = blockIdx.x * 4 + wave;
+  const int nA = E + (Fs > 0 ? 1 + Fs : 0);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T, H]
+
+  const bool router = task <= E && task < nA;  // wave-uniform
+  const float* wrow = task < E ? p.router_w + (size_t)task * H : p.wg;
+  const int n4 = H >> 2;
+  const int f = task - E - 1;
+  const bool shared_task = !router && task < nA;
+  // the task's weights are requested before x is staged
+  float4 w[8];
+  PairW pw;
+  if (router) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = lane + 64 * i;
+      w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else if (shared_task) {
+    load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
+  }
+  stage_x(xs, p.x, (T * H) >> 3);
+  __syncthreads();
+
+  if (router) {
+    float acc[TC];
+#pragma unroll
+    for (int t = 0; t < TC; ++t) acc[t] = 0.0f;
+    for (int j0 = 0; j0 < n4; j0 += 512) {
+      if (j0 > 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = j0 + lane + 64 * i;
+          w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = j0 + lane + 64 * i;
+        if (j < n4) {
+#pragma unroll
+          for (int t = 0; t < TC; ++t) {
+            if (t < T) {
+              const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)t * H + 4 * j);
+              float a = acc[t];
+              a = __builtin_fmaf(bf16_to_f32(xv.x & 0xFFFFu), w[i].x, a);
+              a = __builtin_fmaf(bf16_to_f32(xv.x >> 16), w[i].y, a);
+              a = __builtin_fmaf(bf16_to_f32(xv.y & 0xFFFFu), w[i].z, a);
+              a = __builtin_fmaf(bf16_to_f32(xv.y >> 16), w[i].w, a);
+              acc[t] = a;
+            }
+          }
+        }
+      }
+    }
+    group_reduce<TC, 64>(acc, lane);
+    constexpr int stride = 64 / TC;  // lane l holds token l / stride
+    const int t = lane / stride;
+    if (lane % stride == 0 && t < T) {
+      if (task < E)
+        p.b.logits[(size_t)t * E + task] = acc[0] + (p.router_bias ? p.router_bias[task] : 0.0f);
+      else
+        p.b.logits[(size_t)T * E + t] = acc[0];
+    }
+  } else if (shared_task) {
+    float v[2 * TC];
+    pair_dots<TC>(pw, xs, H, lane, nullptr, T, v);
+    uint16_t* ash = p.b.a + (size_t)TK * F;
+    pair_finish<TC>(v, lane, T, f, ash, [&](int j) { return (size_t)j * Fs; });
+  }
+}
+
+// ============================================================================ B
+// Grid-stride tasks (entry d, row f): one wave per gate row + up row, with the next task's rows
+// requested before the current one is used.
+template <int TC, int NJ>
+__global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint4 smem[];
+  const int T = p.T, H = p.H, E = p.E, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NW = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [T, H]
+  int* sel_idx = reinterpret_cast<int*>(xs + (size_t)T * H);        // [TK]
+  float* sel_w = reinterpret_cast<float*>(sel_idx + TK);            // [TK]
+  int* cnt = reinterpret_cast<int*>(sel_w + TK);                    // [E]
+  unsigned* tmask = reinterpret_cast<unsigned*>(cnt + E);           // [E]
+  int* off = reinterpret_cast<int*>(tmask + E);                     // [E]
+  const Route R = carve_route(off + E, TK, T);
+
+  // logits of this wave's first token requested before x is staged
+  float lv[NJ];
+  if (wave < T) load_logits<NJ>(p.b.logits + (size_t)wave * E, E, lane, lv);
+  stage_x(xs, p.x, (T * H) >> 3);
+  for (int e = tid; e < E; e += 256) {
+    cnt[e] = 0;
+    tmask[e] = 0u;
+  }
+  __syncthreads();
+  for (int t = wave; t < T; t += 4) {
+    if (t != wave) load_logits<NJ>(p.b.logits + (size_t)t * E, E, lane, lv);
+    float my_v, my_w;
+    int my_i;
+    wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w);
+    if (lane < K) {
+      sel_idx[t * K + lane] = my_i;
+      sel_w[t * K + lane] = my_w;
+      atomicAdd(&cnt[my_i], 1);
+      atomicOr(&tmask[my_i], 1u << t);
+    }
+    if (lane == 0 && Fs > 0) R.sgs[t] = 1.0f / (1.0f + __expf(-p.b.logits[(size_t)T * E + t]));
+  }
+  __syncthreads();
+  build_route(R, sel_idx, sel_w, cnt, tmask, off, T, E, K);
+  if (blockIdx.x == 0) {  // the route record for the down projection
+    const int n = (int)route_words(TK, T);
+    for (int i = tid; i < n; i += 256) p.b.route[i] = R.nd[i];
+  }
+  const int D = *R.nd;
+
+  const int nB = D * F;
+  PairW wc, wn;
+  int task = gw;
+  if (task < nB) load_pair(wc, p.gate, p.up, (size_t)R.ent_e[task / F] * F + task % F, H, lane);
+  for (; task < nB; task += NW) {
+    const int nxt = task + NW;
+    if (nxt < nB) load_pair(wn, p.gate, p.up, (size_t)R.ent_e[nxt / F] * F + nxt % F, H, lane);
+    const int d = task / F, f = task % F;
+    const int m = R.ent_m[d], row0 = R.ent_row0[d];
+    float v[2 * TC];
+    pair_dots<TC>(wc, xs, H, lane, R.row_tok + row0, m, v);
+    pair_finish<TC>(v, lane, m, f, p.b.a, [&](int j) { return (size_t)(row0 + j) * F; });
+    if (nxt < nB) wc = wn;
+  }
+}
+
+// ============================================================================ C
+struct DownW {
+  uint4 q;
+  float s, b;
+};
+
+// A_LDS: the activations of the call are staged in LDS (when they fit) instead of being read
+// from global memory for every entry.
+template <int TC, bool A_LDS>
+__global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint4 smem[];
+  const int T = p.T, H = p.H, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sl = lane & 15, grp = lane >> 4;
+  const int NW = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  const size_t a_elems = (size_t)TK * F + (size_t)T * Fs;
+  uint16_t* as = reinterpret_cast<uint16_t*>(smem);                       // [a_elems] if A_LDS
+  const Route R = carve_route(A_LDS ? (void*)(as + a_elems) : (void*)smem, TK, T);
+
+  const int nw = (int)route_words(TK, T);
+  for (int i = tid; i < nw; i += 256) R.nd[i] = p.b.route[i];
+  if (A_LDS)
+    for (size_t v = tid; v < a_elems / 8; v += 256)
+      reinterpret_cast<uint4*>(as)[v] = reinterpret_cast<const uint4*>(p.b.a)[v];
+  __syncthreads();
+  const int D = *R.nd;
+  const int nD = D + (Fs > 0 ? 1 : 0);  // the shared expert is the last entry
+  const uint16_t* abase = A_LDS ? as : p.b.a;
+
+  const int q2 = grp & 1;  // this group takes the entries d = q2, q2 + 2, ...
+  auto load_down = [&](int h, int dfirst, DownW (&dw)[kNB]) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int d = dfirst + 2 * b;
+      dw[b].q = make_uint4(0, 0, 0, 0);
+      dw[b].s = dw[b].b = 0.0f;
+      if (d < nD) {
+        const bool sh = d == D;
+        const int Kd = sh ? Fs : F;
+        if (sl < (Kd >> 5)) {
+          const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
+          const moe_w4_t& W = sh ? p.sh_down : p.down;
+          dw[b].q = reinterpret_cast<const uint4*>(W.q + row * (size_t)(Kd >> 3))[sl];
+          dw[b].s = bf16_to_f32(W.scale[row * (size_t)(Kd >> 6) + (sl >> 1)]);
+          dw[b].b = bf16_to_f32(W.bias[row * (size_t)(Kd >> 6) + (sl >> 1)]);
+        }
+      }
+    }
+  };
+
+  for (int hp = gw; 2 * hp < H; hp += NW) {
+    const int h = 2 * hp + (lane >> 5);
+    float acc = 0.0f;
+    DownW dw[kNB];
+    for (int d0 = q2; d0 < nD; d0 += 2 * kNB) {
+      load_down(h, d0, dw);
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const int d = d0 + 2 * b;
+        if (d >= nD) break;  // uniform across the 16-lane group
+        const bool sh = d == D;
+        const int Kd = sh ? Fs : F;
+        const int m = sh ? T : R.ent_m[d];
+        const int row0 = sh ? 0 : R.ent_row0[d];
+        const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
+        uint32_t wd[16];
+        dequant8(dw[b].q.x, dw[b].s, dw[b].b, wd + 0);
+        dequant8(dw[b].q.y, dw[b].s, dw[b].b, wd + 4);
+        dequant8(dw[b].q.z, dw[b].s, dw[b].b, wd + 8);
+        dequant8(dw[b].q.w, dw[b].s, dw[b].b, wd + 12);
+        float dots[TC];
+#pragma unroll
+        for (int j = 0; j < TC; ++j) {
+          dots[j] = 0.0f;
+          if (j < m && sl < (Kd >> 5)) {
+            const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
+                                    : abase + (size_t)(row0 + j) * F;
+            const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
+            float s = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint4 a4 = av[q];
+              s = dot2_bf16(a4.x, wd[4 * q + 0], s);
+              s = dot2_bf16(a4.y, wd[4 * q + 1], s);
+              s = dot2_bf16(a4.z, wd[4 * q + 2], s);
+              s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+            }
+            dots[j] = s;
+          }
+        }
+        group_reduce<TC, 16>(dots, sl);
+        // lane sl (= token) takes its entry: the token's rank inside this expert
+        int j = 0;
+        bool mine = false;
+        float wgt = 0.0f;
+        if (sl < T && ((tmask >> sl) & 1u)) {
+          j = __popc(tmask & ((1u << sl) - 1u));
+          mine = true;
+          wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
+        }
+        const float val = TC == 1 ? dots[0] : __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
+        if (mine) acc = __builtin_fmaf(wgt, val, acc);
+      }
+    }
+    acc += __shfl_xor(acc, 16, 64);
+    if (q2 == 0 && sl < T) p.out[(size_t)sl * H + h] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------ launcher
+namespace {
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+constexpr size_t kDecLdsMax = 80 * 1024;  // two workgroups per CU (160 KiB of LDS)
+}  // namespace
+
+size_t decode_route_bytes(const Dims& d) { return route_words(d.TK(), d.T) * 4; }
+
+// B's LDS after x: sel_idx, sel_w [TK], cnt, tmask, off [E], the route record, row_tok [TK].
+size_t decode_b_lds_words(const Dims& d) {
+  return 3 * (size_t)d.TK() + 3 * (size_t)d.E + route_words(d.TK(), d.T);
+}
+
+bool decode_fast_ok(const Dims& d) {
+  const size_t lds_b = (size_t)d.T * d.H * 2 + decode_b_lds_words(d) * 4;
+  return d.T >= 1 && d.T <= kDecodeMaxT && d.H <= 2048 && d.F <= 512 && d.Fs <= 512 &&
+         d.E <= 1024 && d.K <= 32 && lds_b <= kDecLdsMax;
+}
+
+hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
+                               const DecodeBufs& b, float* out, hipStream_t s) {
+  DecodeArgs p;
+  p.x = x;
+  p.router_w = desc.router_w;
+  p.router_bias = desc.router_bias;
+  p.wg = d.Fs > 0 ? desc.shared_gate_w : nullptr;
+  p.gate = desc.gate;
+  p.up = desc.up;
+  p.down = desc.down;
+  p.sh_gate = desc.sh_gate;
+  p.sh_up = desc.sh_up;
+  p.sh_down = desc.sh_down;
+  p.T = d.T;
+  p.H = d.H;
+  p.E = d.E;
+  p.K = d.K;
+  p.F = d.F;
+  p.Fs = d.Fs;
+  p.b = b;
+  p.out = out;
+  const size_t lds_x = (size_t)d.T * d.H * 2;
+  const size_t lds_b = lds_x + decode_b_lds_words(d) * 4;
+  const size_t a_bytes = ((size_t)d.TK() * d.F + (size_t)d.T * d.Fs) * 2;
+  const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4;
+  const bool a_lds = a_bytes + lds_c_route <= kDecLdsMax;
+  const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
+  const int nA = d.E + (d.Fs > 0 ? 1 + d.Fs : 0);
+  const dim3 gA((nA + 3) / 4), gB(2 * device_cus()), gC((d.H / 2 + 3) / 4), blk(256);
+#define MOE_DEC(TCV, NJV)                                                        \
+  do {                                                                           \
+    hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x, s, p);                    \
+    hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);               \
+    if (a_lds)                                                                   \
+      hipLaunchKernelGGL((k_dec_c<TCV, true>), gC, blk, lds_c, s, p);            \
+    else                                                                         \
+      hipLaunchKernelGGL((k_dec_c<TCV, false>), gC, blk, lds_c, s, p);           \
+  } while (0)
+#define MOE_DEC_T(NJV) \
+  if (d.T <= 1)        \
+    MOE_DEC(1, NJV);   \
+  else if (d.T <= 2)   \
+    MOE_DEC(2, NJV);   \
+  else if (d.T <= 4)   \
+    MOE_DEC(4, NJV);   \
+  else if (d.T <= 8)   \
+    MOE_DEC(8, NJV);   \
+  else                 \
+    MOE_DEC(16, NJV);
+  if (d.E <= 64) {
+    MOE_DEC_T(1)
+  } else if (d.E <= 256) {
+    MOE_DEC_T(4)
+  } else if (d.E <= 512) {
+    MOE_DEC_T(8)
+  } else {
+    MOE_DEC_T(16)
+  }
+#undef MOE_DEC_T
+#undef MOE_DEC
+  return hipGetLastError();
+}
+
+}  // namespace moe

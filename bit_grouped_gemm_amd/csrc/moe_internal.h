@@ -63,6 +63,16 @@ hipError_t launch_dec_gateup(const Dims& d, const moe_layer_desc_t& desc, const 
 hipError_t launch_dec_down(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* a,
                            const moe_plan_t& plan, const float* topk_w, const float* sgate,
                            float* out, hipStream_t s);
+// Decode path of moe_layer_forward in three launches (decode.hip).
+struct DecodeBufs {
+  float* logits;     // [T, E] router logits, then [T] shared-gate logits
+  int32_t* route;    // per-expert route record handed from the gate/up to the down kernel
+  uint16_t* a;       // [T*K*F] routed activations (grouped rows), then [T*Fs] shared
+};
+bool decode_fast_ok(const Dims& d);
+size_t decode_route_bytes(const Dims& d);
+hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
+                               const DecodeBufs& b, float* out, hipStream_t s);
 hipError_t launch_debug_dequant(const moe_w4_t& w, int n_rows, int kin, int mat, int row,
                                 float* out_f32, uint16_t* out_bf16, hipStream_t s);
 
@@ -144,47 +154,105 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Top-k of one token's E logits by one wave (E <= 64*NJ): lane l holds logits e = l + 64*j.
-// K rounds of a wave arg-max ordered by (larger logit, then lower expert index); lane r ends
-// with the rank-r winner (my_v, my_i), lanes >= K with -inf.
+// Value of the butterfly partner lane at distance O (1, 2, 4 or 8) inside a row of 16 lanes,
+// through DPP (no LDS round trip): quad_perm swaps for O = 1, 2, the half-row mirror for O = 4
+// and the row mirror for O = 8. The partner always differs from the lane in bit log2(O) (the
+// mirrors pair i with 7-i and 15-i), so a halving butterfly over these pairs still ends with
+// lane r holding the entries selected by r's bits.
+template <int O>
+__device__ __forceinline__ float dpp_partner16(float v) {
+  constexpr int ctrl = O == 8 ? 0x140 : (O == 4 ? 0x141 : (O == 2 ? 0x4E : 0xB1));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum of v over the 64 lanes: DPP row shifts inside rows of 16 (lanes whose
+// source falls outside the row add 0), then the totals of the lower rows read from lanes 15,
+// 31, 47.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Maximum of v over the wave, returned to every lane. Rows of 16 lanes reduce with DPP row
+// shifts (no LDS round trip); the four row maxima are read from lanes 15, 31, 47, 63.
+__device__ __forceinline__ float wave_max(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Top-k of one token's E logits by one wave (E <= 64*NJ) with the softmax over the selected
+// logits. Lane l holds logits e = l + 64*j in v[j]. Each of the K rounds takes the wave maximum
+// M of the remaining logits; the winner is the lowest expert index whose logit equals M (one
+// ballot per j: for fixed j the lanes are in expert order, and j-blocks ascend). Lane r < K ends
+// with the rank-r expert my_i, its logit my_v and its renormalised weight
+// my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank order; lanes >= K get
+// my_w = 0.
 template <int NJ>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lt, int E, int K, int lane,
-                                          float& my_v, int& my_i) {
-  float v[NJ];
+__device__ __forceinline__ void wave_topk_softmax(const float (&v)[NJ], int E, int K, int lane,
+                                                  float& my_v, int& my_i, float& my_w) {
+  uint32_t avail = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (lane + 64 * j < E) avail |= 1u << j;
+  my_v = -INFINITY;
+  my_i = 0;
+  float my_z = 0.0f, m0 = 0.0f, den = 0.0f;
+  for (int r = 0; r < K; ++r) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if ((avail >> j) & 1u) lm = fmaxf(lm, v[j]);
+    const float M = wave_max(lm);
+    int win = -1;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint64_t b = __ballot(((avail >> j) & 1u) && v[j] == M);
+      if (win < 0 && b != 0) win = (int)__builtin_ctzll(b) + 64 * j;
+    }
+    if ((win & 63) == lane) avail &= ~(1u << (win >> 6));
+    if (r == 0) m0 = M;
+    const float z = __expf(M - m0);
+    den += z;
+    if (lane == r) {
+      my_v = M;
+      my_i = win;
+      my_z = z;
+    }
+  }
+  my_w = lane < K ? my_z / den : 0.0f;
+}
+
+template <int NJ>
+__device__ __forceinline__ void load_logits(const float* __restrict__ lt, int E, int lane,
+                                            float (&v)[NJ]) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < E ? lt[e] : -INFINITY;
   }
-  uint32_t taken = 0;
-  my_v = -INFINITY;
-  my_i = 0;
-  for (int r = 0; r < K; ++r) {
-    float best = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u) && (v[j] > best || (v[j] == best && e < bi))) {
-        best = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(best, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > best || (ov == best && oi < bi)) {
-        best = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == r) {
-      my_v = best;
-      my_i = bi;
-    }
-  }
+}
+
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lt, int E, int K, int lane,
+                                          float& my_v, int& my_i, float& my_w) {
+  float v[NJ];
+  load_logits<NJ>(lt, E, lane, v);
+  wave_topk_softmax<NJ>(v, E, K, lane, my_v, my_i, my_w);
 }
 
 // x . wg for one token (bf16 x, fp32 wg), by one wave: lane l takes the contiguous inputs

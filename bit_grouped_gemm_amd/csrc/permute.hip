@@ -164,13 +164,11 @@ __global__ __launch_bounds__(1024) void k_route_small(
   float my_v = -INFINITY;
   int my_i = 0;
   if (t < T) {
-    wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i);
-    const float vmax = __shfl(my_v, 0, 64);
-    const float z = lane < K ? __expf(my_v - vmax) : 0.0f;
-    const float den = wave_sum(z);
+    float my_w;
+    wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i, my_w);
     if (lane < K) {
       idx[t * K + lane] = my_i;
-      wout[t * K + lane] = z / den;
+      wout[t * K + lane] = my_w;
       atomicAdd(&cnt[my_i], 1);
       atomicOr(&mask[my_i], 1u << t);
     }

@@ -205,15 +205,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // no barriers in this kernel
-  float my_v;
+  float my_v, my_w;
   int my_i;
-  wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i);
-  const float vmax = __shfl(my_v, 0, 64);
-  const float z = lane < K ? __expf(my_v - vmax) : 0.0f;
-  const float den = wave_sum(z);
+  wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i, my_w);
   if (lane < K) {
     idx[(size_t)t * K + lane] = my_i;
-    wout[(size_t)t * K + lane] = z / den;
+    wout[(size_t)t * K + lane] = my_w;
   }
   if (wg != nullptr) {
     const float g = shared_gate_logit(x + (size_t)t * H, wg, H, lane);

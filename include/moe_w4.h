@@ -25,7 +25,8 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned, owned by the caller;
  *     the library keeps no pointer after a call returns and allocates no device memory.
- *     Scratch memory comes from a caller workspace sized by moe_workspace_bytes().
+ *     Scratch memory comes from a caller workspace sized by moe_workspace_bytes() and
+ *     256-byte aligned; its contents need no initialisation and are not kept between calls.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls validate
  *     their arguments on the host, then only enqueue work: no host synchronisation, no
  *     device-to-host copy, so the sequence can be captured into a HIP graph. Results are
@@ -180,9 +181,12 @@ int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t
                 const float* topk_w, const float* shared_y, const float* shared_gate,
                 int32_t T, float* out, void* stream);
 
-/* The whole layer: x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path
- * (bandwidth-bound GEMV kernels that stream only the selected experts' weights, with the
- * combine fused into the down projection), larger T the prefill path (MFMA grouped GEMM).
+/* The whole layer: x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path, larger T
+ * the prefill path (MFMA grouped GEMM). For H <= 2048 and F, Fs <= 512 the decode path is three
+ * launches: (router logits + the shared expert's gate/up), (top-k in every workgroup + the
+ * selected experts' gate/up), (down projection fused with the weighted combine); each selected
+ * expert's weights are streamed once with 16-byte loads, and the combine is deterministic.
+ * Other decode shapes run the same steps as separate GEMV kernels.
  * flags: MOE_FLAG_*. workspace: moe_workspace_bytes(desc, T, flags). */
 int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
                       void* workspace, size_t ws_bytes, int32_t flags, void* stream);

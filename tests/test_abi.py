@@ -109,6 +109,8 @@ def test_call_rejections_before_launch():
     assert forward(d, 64, need, flags=8) == M.MOE_INVALID_ARG
     assert forward(d, 64, need, x=FAKE + 2) == M.MOE_INVALID_ARG
     assert forward(d, 64, need, out=None) == M.MOE_INVALID_ARG
+    assert M.lib().moe_layer_forward(ctypes.byref(d), FAKE, 64, FAKE, FAKE + 16, need, 0, None) \
+        == M.MOE_INVALID_ARG                                   # workspace must be 256-byte aligned
     L = M.lib()
     assert L.moe_route(ctypes.byref(d), FAKE, 4, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) \
         == M.MOE_INVALID_ARG                                   # shared_gate needed when Fs > 0
@@ -130,3 +132,4 @@ def test_call_rejections_before_launch():
         == M.MOE_INVALID_ARG                                   # row out of range
     assert L.moe_debug_dequant_w4(ctypes.byref(w), 4, 96, 0, 0, FAKE, None, None) \
         == M.MOE_UNSUPPORTED
+

@@ -105,7 +105,25 @@ def test_zero_tokens_is_a_noop():
     assert torch.all(out == 3.0)
 
 
-@pytest.mark.parametrize("name,T,flags", [("full", 1, 0), ("mid", 300, 0), ("mid", 300, ATOMIC)])
+def test_decode_workspace_reuse_across_shapes():
+    """One workspace serves decode calls of different T back to back."""
+    import torch
+    from bit_grouped_gemm_amd import moe_w4 as M
+    layer = device_layer("full")
+    ws = M.alloc_workspace(layer, 16)
+    host = host_layer("full")
+    for T in (16, 1, 3, 8, 1):
+        xh, x = tokens("full", T, stream=20 + T)
+        out = torch.empty((T, layer.H), dtype=torch.float32, device=DEV)
+        M.moe_layer_forward(layer, x, out, ws)
+        torch.cuda.synchronize()
+        gidx = gpu_routing(layer, x, T)
+        ref, ref_exact, ties, swapped = oracle_reference("full", host, xh, layer.K, gpu_idx=gidx)
+        check("full", T, 0, out.cpu().numpy(), ref, ref_exact, ties, swapped, " reused ws")
+
+
+@pytest.mark.parametrize("name,T,flags", [("full", 1, 0), ("full", 8, 0), ("mid", 300, 0),
+                                          ("mid", 300, ATOMIC)])
 def test_graph_replays_match_eager(name, T, flags):
     """The layer captured into a HIP graph (as the benchmark runs it) replays correctly,
     several times, with eager work and synchronisations between the replays."""

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 from gpu_common import DEV, device_layer, host_layer, log, tokens
+import synth
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -126,3 +127,37 @@ def test_permute_flags_invalid_expert_ids():
     torch.cuda.synchronize()
     assert int(plan["num_blocks"].cpu().item()) == -1
     assert int(plan["counts"].cpu().numpy().sum()) == T * K - 1
+
+
+def test_route_negative_logits_and_exact_ties():
+    """Every logit far below zero (router bias -60) and exact ties (duplicated router rows):
+    the selection must not treat zero as a floor, and equal logits go to the lower expert index.
+    Checked through moe_route and through the layer's decode and prefill paths."""
+    import torch
+    from bit_grouped_gemm_amd import moe_w4 as M
+    from gpu_common import TOL_MAX_REL, TOL_MEAN_ABS
+    base = host_layer("mid")
+    host = dict(base)
+    rw = base["router_w"].copy()
+    for a, b in ((4, 5), (3, 17), (31, 30), (0, 9)):
+        rw[b] = rw[a]          # expert b scores exactly like expert a
+    host["router_w"] = rw
+    host["router_bias"] = np.full(rw.shape[0], -60.0, np.float32)
+    s = synth.SHAPES["mid"]
+    layer = M.upload_layer(host, s.H, s.E, s.K, s.F, s.Fs, device=DEV)
+    for T in (1, 8, 300):
+        xh, x = tokens("mid", T, stream=40)
+        gi, gw, _, _ = route(layer, x, T)
+        logits = O.router_logits(xh, host["router_w"], host["router_bias"])
+        assert logits.max() < -50
+        ridx, rp = O.select_topk(logits, layer.K)
+        assert np.array_equal(gi, ridx), T
+        assert np.abs(gw - rp).max() < 5e-6
+        for flags in (0, M.MOE_FLAG_FORCE_PREFILL):
+            ws = M.alloc_workspace(layer, T, flags)
+            out = torch.empty((T, s.H), dtype=torch.float32, device=DEV)
+            M.moe_layer_forward(layer, x, out, ws, flags)
+            torch.cuda.synchronize()
+            st = O.error_stats(out.cpu().numpy(), O.layer_forward(host, xh, layer.K, "bf16"))
+            log(f"[route] ties/negative T={T} flags={flags}: {st}")
+            assert st["max_rel"] <= TOL_MAX_REL and st["mean_abs"] <= TOL_MEAN_ABS
