@@ -79,7 +79,7 @@ __device__ __forceinline__ void group_reduce(float (&v)[N], int r) {
 // 16-byte load per row and lane, a 1 KiB row per wave).
 struct PairW {
   uint4 g, u;
-  float gs, gb, us, ub;
+  uint32_t gs, gb, us, ub;  // raw bf16 bits: converted when used, so a prefetch never waits
 };
 
 __device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe_w4_t& U,
@@ -88,13 +88,13 @@ __device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe
     const size_t sidx = row * (size_t)(H >> 6) + (lane >> 1);
     w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[lane];
     w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[lane];
-    w.gs = bf16_to_f32(G.scale[sidx]);
-    w.gb = bf16_to_f32(G.bias[sidx]);
-    w.us = bf16_to_f32(U.scale[sidx]);
-    w.ub = bf16_to_f32(U.bias[sidx]);
+    w.gs = G.scale[sidx];
+    w.gb = G.bias[sidx];
+    w.us = U.scale[sidx];
+    w.ub = U.bias[sidx];
   } else {
     w.g = w.u = make_uint4(0, 0, 0, 0);
-    w.gs = w.gb = w.us = w.ub = 0.0f;
+    w.gs = w.gb = w.us = w.ub = 0u;
   }
 }
 
@@ -108,14 +108,16 @@ __device__ __forceinline__ void pair_dots(const PairW& w, const uint16_t* xs, in
   for (int j = 0; j < 2 * TC; ++j) v[j] = 0.0f;
   if (lane >= (H >> 5)) return;
   uint32_t dg[16], du[16];
-  dequant8(w.g.x, w.gs, w.gb, dg + 0);
-  dequant8(w.g.y, w.gs, w.gb, dg + 4);
-  dequant8(w.g.z, w.gs, w.gb, dg + 8);
-  dequant8(w.g.w, w.gs, w.gb, dg + 12);
-  dequant8(w.u.x, w.us, w.ub, du + 0);
-  dequant8(w.u.y, w.us, w.ub, du + 4);
-  dequant8(w.u.z, w.us, w.ub, du + 8);
-  dequant8(w.u.w, w.us, w.ub, du + 12);
+  const float gs = bf16_to_f32(w.gs), gb = bf16_to_f32(w.gb);
+  const float us = bf16_to_f32(w.us), ub = bf16_to_f32(w.ub);
+  dequant8(w.g.x, gs, gb, dg + 0);
+  dequant8(w.g.y, gs, gb, dg + 4);
+  dequant8(w.g.z, gs, gb, dg + 8);
+  dequant8(w.g.w, gs, gb, dg + 12);
+  dequant8(w.u.x, us, ub, du + 0);
+  dequant8(w.u.y, us, ub, du + 4);
+  dequant8(w.u.z, us, ub, du + 8);
+  dequant8(w.u.w, us, ub, du + 12);
 #pragma unroll
   for (int j = 0; j < TC; ++j) {
     if (j < m) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
 // ============================================================================ C
 struct DownW {
   uint4 q;
-  float s, b;
+  uint32_t s, b;  // raw bf16 bits
 };
 
 // A_LDS: the activations of the call are staged in LDS (when they fit) instead of being read
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
     for (int b = 0; b < kNB; ++b) {
       const int d = dfirst + 2 * b;
       dw[b].q = make_uint4(0, 0, 0, 0);
-      dw[b].s = dw[b].b = 0.0f;
+      dw[b].s = dw[b].b = 0u;
       if (d < nD) {
         const bool sh = d == D;
         const int Kd = sh ? Fs : F;
@@ -424,8 +426,8 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
           const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
           const moe_w4_t& W = sh ? p.sh_down : p.down;
           dw[b].q = reinterpret_cast<const uint4*>(W.q + row * (size_t)(Kd >> 3))[sl];
-          dw[b].s = bf16_to_f32(W.scale[row * (size_t)(Kd >> 6) + (sl >> 1)]);
-          dw[b].b = bf16_to_f32(W.bias[row * (size_t)(Kd >> 6) + (sl >> 1)]);
+          dw[b].s = W.scale[row * (size_t)(Kd >> 6) + (sl >> 1)];
+          dw[b].b = W.bias[row * (size_t)(Kd >> 6) + (sl >> 1)];
         }
       }
     }
@@ -447,10 +449,11 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
         const int row0 = sh ? 0 : R.ent_row0[d];
         const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
         uint32_t wd[16];
-        dequant8(dw[b].q.x, dw[b].s, dw[b].b, wd + 0);
-        dequant8(dw[b].q.y, dw[b].s, dw[b].b, wd + 4);
-        dequant8(dw[b].q.z, dw[b].s, dw[b].b, wd + 8);
-        dequant8(dw[b].q.w, dw[b].s, dw[b].b, wd + 12);
+        const float ds = bf16_to_f32(dw[b].s), db = bf16_to_f32(dw[b].b);
+        dequant8(dw[b].q.x, ds, db, wd + 0);
+        dequant8(dw[b].q.y, ds, db, wd + 4);
+        dequant8(dw[b].q.z, ds, db, wd + 8);
+        dequant8(dw[b].q.w, ds, db, wd + 12);
         float dots[TC];
 #pragma unroll
         for (int j = 0; j < TC; ++j) {

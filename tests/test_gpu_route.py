@@ -102,12 +102,13 @@ def test_permute_matches_oracle(E, K, T, Fs, skew):
     assert np.array_equal(plan["offsets"].cpu().numpy(), offsets)
     assert np.array_equal(plan["sorted_slots"].cpu().numpy()[:TK], sorted_slots)
     assert np.array_equal(plan["slot_pos"].cpu().numpy()[:TK], slot_pos)
-    # block map: tiles of at most 128 rows per non-empty expert in expert order, then the
-    # shared expert's T rows
-    want = [(e, m0, min(128, int(counts[e]) - m0), int(offsets[e]) + m0)
-            for e in range(E) for m0 in range(0, int(counts[e]), 128)]
+    # block map: tiles of at most MOE_BLOCK_M rows per non-empty expert in expert order, then
+    # the shared expert's T rows
+    BM = M.MOE_BLOCK_M
+    want = [(e, m0, min(BM, int(counts[e]) - m0), int(offsets[e]) + m0)
+            for e in range(E) for m0 in range(0, int(counts[e]), BM)]
     if Fs > 0:
-        want += [(E, m0, min(128, T - m0), TK + m0) for m0 in range(0, T, 128)]
+        want += [(E, m0, min(BM, T - m0), TK + m0) for m0 in range(0, T, BM)]
     nb = int(plan["num_blocks"].cpu().item())
     got = [tuple(r) for r in plan["blocks"].cpu().numpy().reshape(-1, 4)[:nb].tolist()]
     assert nb == len(want) and got == want
