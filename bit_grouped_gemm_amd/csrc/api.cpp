@@ -164,6 +164,77 @@ bool plan_ok(const moe_plan_t* p) {
          p->num_blocks && aligned(p->blocks, 16);
 }
 
+
+// The launch sequence of moe_layer_forward. phase == -1 enqueues all of it, phase >= 0 only
+// launch `phase`, phase == -2 enqueues nothing; *nphases (if given) receives the count.
+//   decode, one-pass kernels: 0 router + shared expert, 1 top-k + routed gate/up,
+//                             2 down + combine
+//   decode, other shapes:     0 router, 1 top-k + permutation, 2 gate/up, 3 down + combine
+//   prefill:                  0 router, 1 top-k, 2 permutation, 3 gate/up GEMM,
+//                             4 down GEMM, 5 combine   (atomic: 4 zero fill, 5 down + combine)
+int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, float* out,
+                   void* ws, const Layout& L, int flags, hipStream_t s, int phase,
+                   int* nphases) {
+  int k = 0;
+  hipError_t err = hipSuccess;
+  auto step = [&](auto&& launch) {
+    if (err == hipSuccess && (phase == -1 || phase == k)) err = launch();
+    ++k;
+  };
+  const bool decode = use_decode(d, flags);
+  int32_t* idx = at<int32_t>(ws, L.topk_idx);
+  float* w = at<float>(ws, L.topk_w);
+  float* sgate = at<float>(ws, L.sgate);
+  float* logits = at<float>(ws, L.logits);
+  moe_plan_t plan{at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                  at<int32_t>(ws, L.sorted),  at<int32_t>(ws, L.slotpos),
+                  at<int32_t>(ws, L.blocks),  at<int32_t>(ws, L.nblk)};
+  uint16_t* a = at<uint16_t>(ws, L.a);
+  const int mb = max_blocks(d);
+  const float* wg = d.Fs > 0 ? desc->shared_gate_w : nullptr;
+
+  if (decode && decode_fast_ok(d)) {
+    const DecodeBufs b{logits, at<int32_t>(ws, L.droute), a};
+    for (int ph = 0; ph < 3; ++ph)
+      step([&] { return launch_decode_layer(d, *desc, x, b, out, s, ph); });
+  } else if (decode) {
+    step([&] { return launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E,
+                                                d.H, logits, s); });
+    step([&] { return launch_route_small(logits, x, wg, d, idx, w, sgate, plan, s); });
+    step([&] { return launch_dec_gateup(d, *desc, x, plan, mb, a, s); });
+    step([&] { return launch_dec_down(d, *desc, a, plan, w, sgate, out, s); });
+  } else {
+    step([&] { return launch_router_logits_mfma(x, desc->router_w, desc->router_bias, d.T, d.E,
+                                                d.H, logits, s); });
+    step([&] { return launch_topk(logits, x, wg, d.T, d.E, d.K, d.H, idx, w, sgate, s); });
+    step([&] { return launch_permute(idx, d, d.Fs > 0, at<int32_t>(ws, L.hist), plan, s); });
+    step([&] {
+      const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);
+      return launch_gemm_w4(kGateUp, pg, mb, s);
+    });
+    if (flags & MOE_FLAG_ATOMIC_COMBINE) {
+      step([&] { return launch_fill_zero(out, (size_t)d.T * d.H, s); });
+      step([&] {
+        const GemmParams pd =
+            gemm_params(desc, d, MOE_GEMM_DOWN_COMBINE_ATOMIC, a, &plan, w, sgate, out);
+        return launch_gemm_w4(kDownAtomic, pd, mb, s);
+      });
+    } else {
+      float* y = at<float>(ws, L.y);
+      step([&] {
+        const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN, a, &plan, nullptr, nullptr, y);
+        return launch_gemm_w4(kDownStore, pd, mb, s);
+      });
+      step([&] {
+        return launch_combine(y, plan.slot_pos, w, d.Fs > 0 ? y + (size_t)d.TK() * d.H : nullptr,
+                              sgate, d, out, s);
+      });
+    }
+  }
+  if (nphases) *nphases = k;
+  return hip_status(err);
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,6 +361,21 @@ int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t
 
 int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
                       void* workspace, size_t ws_bytes, int32_t flags, void* stream) {
+  return moe_layer_forward_phase(desc, x, T, out, workspace, ws_bytes, flags, -1, stream);
+}
+
+int32_t moe_layer_num_phases(const moe_layer_desc_t* desc, int32_t T, int32_t flags) {
+  if (check_desc(desc) != MOE_OK || T <= 0) return 0;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return 0;
+  int n = 0;
+  layer_sequence(desc, d, nullptr, nullptr, nullptr, layout_of(d, flags), flags, nullptr, -2, &n);
+  return n;
+}
+
+int moe_layer_forward_phase(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T,
+                            float* out, void* workspace, size_t ws_bytes, int32_t flags,
+                            int32_t phase, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (T < 0 || (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_FORCE_PREFILL))) return MOE_INVALID_ARG;
@@ -300,51 +386,65 @@ int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T
     return MOE_INVALID_ARG;
   const Layout L = layout_of(d, flags);
   if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
+  if (phase >= 0 && phase >= moe_layer_num_phases(desc, T, flags)) return MOE_INVALID_ARG;
+  if (phase < -1) return MOE_INVALID_ARG;
+  return layer_sequence(desc, d, x, out, workspace, L, flags, static_cast<hipStream_t>(stream),
+                        phase, nullptr);
+}
+
+int moe_residual_rmsnorm(const float* y, float* resid, uint16_t* x_out, int32_t T, int32_t H,
+                         float eps, int32_t init, void* stream) {
+  if (T < 0 || H <= 0 || H % 64 || H > 16384 || !(eps >= 0.0f) || (init != 0 && init != 1))
+    return MOE_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!resid || !aligned(resid, 16) || !x_out || !aligned(x_out, 16)) return MOE_INVALID_ARG;
+  if (!init && (!y || !aligned(y, 16))) return MOE_INVALID_ARG;
+  return hip_status(launch_residual_rmsnorm(y, resid, x_out, T, H, eps, init,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_stack_workspace_bytes(const moe_layer_desc_t* const* layers, int32_t n_layers,
+                                 int32_t T_max, int32_t flags) {
+  if (!layers || n_layers <= 0 || T_max < 0) return 0;
+  size_t need = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const size_t w = moe_workspace_bytes(layers[l], T_max, flags);
+    if (w == 0) return 0;
+    if (layers[l]->hidden != layers[0]->hidden) return 0;
+    if (w > need) need = w;
+  }
+  // the layer workspace, then the layer output y [T_max, H] fp32
+  return align_up(need) + align_up((size_t)T_max * layers[0]->hidden * 4);
+}
+
+int moe_stack_forward(const moe_layer_desc_t* const* layers, int32_t n_layers, float* resid,
+                      uint16_t* x, int32_t T, float eps, void* workspace, size_t ws_bytes,
+                      int32_t flags, void* stream) {
+  if (!layers || n_layers <= 0 || T < 0 || !(eps >= 0.0f)) return MOE_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    const int st = check_desc(layers[l]);
+    if (st != MOE_OK) return st;
+    if (layers[l]->hidden != layers[0]->hidden) return MOE_INVALID_ARG;
+  }
+  if (T == 0) return MOE_OK;
+  const int H = layers[0]->hidden;
+  if (!resid || !aligned(resid, 16) || !x || !aligned(x, 16) || !workspace ||
+      !aligned(workspace, 256))
+    return MOE_INVALID_ARG;
+  const size_t need = moe_stack_workspace_bytes(layers, n_layers, T, flags);
+  if (need == 0) return MOE_UNSUPPORTED;
+  if (ws_bytes < need) return MOE_WORKSPACE_TOO_SMALL;
+  const size_t lws = need - align_up((size_t)T * H * 4);
+  float* y = at<float>(workspace, lws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool decode = use_decode(d, flags);
-
-  int32_t* idx = at<int32_t>(workspace, L.topk_idx);
-  float* w = at<float>(workspace, L.topk_w);
-  float* sgate = at<float>(workspace, L.sgate);
-  moe_plan_t plan{at<int32_t>(workspace, L.counts), at<int32_t>(workspace, L.offsets),
-                  at<int32_t>(workspace, L.sorted),  at<int32_t>(workspace, L.slotpos),
-                  at<int32_t>(workspace, L.blocks),  at<int32_t>(workspace, L.nblk)};
-  uint16_t* a = at<uint16_t>(workspace, L.a);
-  const int mb = max_blocks(d);
-
-  if (decode && decode_fast_ok(d)) {
-    // three launches: router + shared expert, top-k + routed gate/up, down + combine
-    const DecodeBufs b{at<float>(workspace, L.logits), at<int32_t>(workspace, L.droute), a};
-    return hip_status(launch_decode_layer(d, *desc, x, b, out, s));
-  }
-  if (decode) {
-    // router GEMV, then top-k + permutation + block map in one workgroup, then the two GEMVs
-    float* logits = at<float>(workspace, L.logits);
-    if (launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits,
-                                  s) != hipSuccess)
-      return MOE_HIP_ERROR;
-    if (launch_route_small(logits, x, d.Fs > 0 ? desc->shared_gate_w : nullptr, d, idx, w, sgate,
-                           plan, s) != hipSuccess)
-      return MOE_HIP_ERROR;
-    if (launch_dec_gateup(d, *desc, x, plan, mb, a, s) != hipSuccess) return MOE_HIP_ERROR;
-    return hip_status(launch_dec_down(d, *desc, a, plan, w, sgate, out, s));
-  }
-  st = run_route(desc, d, x, idx, w, sgate, workspace, L, decode, s);
-  if (st != MOE_OK) return st;
-  if (launch_permute(idx, d, d.Fs > 0, at<int32_t>(workspace, L.hist), plan, s) != hipSuccess)
+  if (launch_residual_rmsnorm(nullptr, resid, x, T, H, eps, 1, s) != hipSuccess)
     return MOE_HIP_ERROR;
-  const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);
-  if (launch_gemm_w4(kGateUp, pg, mb, s) != hipSuccess) return MOE_HIP_ERROR;
-  if (flags & MOE_FLAG_ATOMIC_COMBINE) {
-    if (launch_fill_zero(out, (size_t)d.T * d.H, s) != hipSuccess) return MOE_HIP_ERROR;
-    const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN_COMBINE_ATOMIC, a, &plan, w, sgate, out);
-    return hip_status(launch_gemm_w4(kDownAtomic, pd, mb, s));
+  for (int l = 0; l < n_layers; ++l) {
+    int st = moe_layer_forward(layers[l], x, T, y, workspace, lws, flags, stream);
+    if (st != MOE_OK) return st;
+    if (launch_residual_rmsnorm(y, resid, x, T, H, eps, 0, s) != hipSuccess) return MOE_HIP_ERROR;
   }
-  float* y = at<float>(workspace, L.y);
-  const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN, a, &plan, nullptr, nullptr, y);
-  if (launch_gemm_w4(kDownStore, pd, mb, s) != hipSuccess) return MOE_HIP_ERROR;
-  return hip_status(launch_combine(y, plan.slot_pos, w,
-                                   d.Fs > 0 ? y + (size_t)d.TK() * d.H : nullptr, sgate, d, out, s));
+  return MOE_OK;
 }
 
 int moe_debug_dequant_w4(const moe_w4_t* w, int32_t n_rows, int32_t Kin, int32_t mat,

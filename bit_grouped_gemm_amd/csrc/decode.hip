@@ -524,7 +524,7 @@ bool decode_fast_ok(const Dims& d) {
 }
 
 hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
-                               const DecodeBufs& b, float* out, hipStream_t s) {
+                               const DecodeBufs& b, float* out, hipStream_t s, int phase) {
   DecodeArgs p;
   p.x = x;
   p.router_w = desc.router_w;
@@ -554,12 +554,16 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const dim3 gA((nA + 3) / 4), gB(2 * device_cus()), gC((d.H / 2 + 3) / 4), blk(256);
 #define MOE_DEC(TCV, NJV)                                                        \
   do {                                                                           \
-    hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x, s, p);                    \
-    hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);               \
-    if (a_lds)                                                                   \
-      hipLaunchKernelGGL((k_dec_c<TCV, true>), gC, blk, lds_c, s, p);            \
-    else                                                                         \
-      hipLaunchKernelGGL((k_dec_c<TCV, false>), gC, blk, lds_c, s, p);           \
+    if (phase < 0 || phase == 0)                                                 \
+      hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x, s, p);                  \
+    if (phase < 0 || phase == 1)                                                 \
+      hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);             \
+    if (phase < 0 || phase == 2) {                                               \
+      if (a_lds)                                                                 \
+        hipLaunchKernelGGL((k_dec_c<TCV, true>), gC, blk, lds_c, s, p);          \
+      else                                                                       \
+        hipLaunchKernelGGL((k_dec_c<TCV, false>), gC, blk, lds_c, s, p);         \
+    }                                                                            \
   } while (0)
 #define MOE_DEC_T(NJV) \
   if (d.T <= 1)        \

@@ -71,8 +71,11 @@ struct DecodeBufs {
 };
 bool decode_fast_ok(const Dims& d);
 size_t decode_route_bytes(const Dims& d);
+// phase < 0: all three launches; 0, 1, 2: only that one.
 hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
-                               const DecodeBufs& b, float* out, hipStream_t s);
+                               const DecodeBufs& b, float* out, hipStream_t s, int phase);
+hipError_t launch_residual_rmsnorm(const float* y, float* r, uint16_t* x, int T, int H, float eps,
+                                   int init, hipStream_t s);
 hipError_t launch_debug_dequant(const moe_w4_t& w, int n_rows, int kin, int mat, int row,
                                 float* out_f32, uint16_t* out_bf16, hipStream_t s);
 

@@ -24,7 +24,9 @@ DECODE_MAX_T = 16
 
 EXPORTS = ("moe_status_str", "moe_version", "moe_workspace_bytes", "moe_plan_max_blocks",
            "moe_route", "moe_permute", "moe_grouped_gemm_w4", "moe_combine",
-           "moe_layer_forward", "moe_debug_dequant_w4")
+           "moe_layer_forward", "moe_debug_dequant_w4", "moe_layer_num_phases",
+           "moe_layer_forward_phase", "moe_residual_rmsnorm", "moe_stack_workspace_bytes",
+           "moe_stack_forward")
 
 
 class W4(ctypes.Structure):
@@ -79,6 +81,17 @@ def lib():
     L.moe_combine.argtypes = [pdesc, vp, vp, vp, vp, vp, i32, vp, vp]
     L.moe_layer_forward.restype = ctypes.c_int
     L.moe_layer_forward.argtypes = [pdesc, vp, i32, vp, vp, sz, i32, vp]
+    L.moe_layer_num_phases.restype = i32
+    L.moe_layer_num_phases.argtypes = [pdesc, i32, i32]
+    L.moe_layer_forward_phase.restype = ctypes.c_int
+    L.moe_layer_forward_phase.argtypes = [pdesc, vp, i32, vp, vp, sz, i32, i32, vp]
+    L.moe_residual_rmsnorm.restype = ctypes.c_int
+    L.moe_residual_rmsnorm.argtypes = [vp, vp, vp, i32, i32, ctypes.c_float, i32, vp]
+    ppdesc = ctypes.POINTER(pdesc)
+    L.moe_stack_workspace_bytes.restype = sz
+    L.moe_stack_workspace_bytes.argtypes = [ppdesc, i32, i32, i32]
+    L.moe_stack_forward.restype = ctypes.c_int
+    L.moe_stack_forward.argtypes = [ppdesc, i32, vp, vp, i32, ctypes.c_float, vp, sz, i32, vp]
     L.moe_debug_dequant_w4.restype = ctypes.c_int
     L.moe_debug_dequant_w4.argtypes = [ctypes.POINTER(W4), i32, i32, i32, i32, vp, vp, vp]
     _lib = L
@@ -234,3 +247,48 @@ def moe_debug_dequant_w4(w4: tuple, n_rows: int, kin: int, mat: int, row: int, o
     st = W4(q.data_ptr(), s.data_ptr(), b.data_ptr())
     _check(lib().moe_debug_dequant_w4(ctypes.byref(st), n_rows, kin, mat, row, _p(out_f32),
                                       _p(out_bf16), _stream(stream)), "moe_debug_dequant_w4")
+
+
+def moe_layer_num_phases(layer, T: int, flags: int = 0) -> int:
+    return lib().moe_layer_num_phases(layer.desc_ptr, T, flags)
+
+
+def moe_layer_forward_phase(layer, x, out, workspace, phase: int, flags: int = 0, stream=None):
+    _check(lib().moe_layer_forward_phase(layer.desc_ptr, _p(x), x.shape[0], _p(out), _p(workspace),
+                                         workspace.numel(), flags, phase, _stream(stream)),
+           "moe_layer_forward_phase")
+
+
+RMS_EPS = 1e-6
+
+
+def moe_residual_rmsnorm(y, resid, x, init: bool = False, eps: float = RMS_EPS, stream=None):
+    T, H = resid.shape
+    _check(lib().moe_residual_rmsnorm(_p(y), _p(resid), _p(x), T, H, eps, 1 if init else 0,
+                                      _stream(stream)), "moe_residual_rmsnorm")
+
+
+class Stack:
+    """A stack of device layers for moe_stack_forward (keeps the descriptor array alive)."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        arr = (ctypes.POINTER(LayerDesc) * len(self.layers))()
+        for i, l in enumerate(self.layers):
+            arr[i] = ctypes.pointer(l.desc)
+        self._arr = arr
+
+    def workspace_bytes(self, T_max: int, flags: int = 0) -> int:
+        n = lib().moe_stack_workspace_bytes(self._arr, len(self.layers), T_max, flags)
+        if n == 0:
+            raise MoEError(MOE_UNSUPPORTED, "moe_stack_workspace_bytes")
+        return n
+
+    def alloc_workspace(self, T_max: int, flags: int = 0, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes(T_max, flags), dtype=torch.uint8, device=device)
+
+    def forward(self, resid, x, workspace, flags: int = 0, eps: float = RMS_EPS, stream=None):
+        _check(lib().moe_stack_forward(self._arr, len(self.layers), _p(resid), _p(x), x.shape[0],
+                                       eps, _p(workspace), workspace.numel(), flags,
+                                       _stream(stream)), "moe_stack_forward")

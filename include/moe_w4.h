@@ -191,6 +191,44 @@ int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t
 int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
                       void* workspace, size_t ws_bytes, int32_t flags, void* stream);
 
+/* moe_layer_forward as its sequence of kernel launches, one launch per call, for measuring
+ * and checking the kernels one at a time. moe_layer_num_phases(desc, T, flags) gives the
+ * number of launches for this T and these flags (0 if the arguments are invalid); calling
+ * moe_layer_forward_phase for phases 0, 1, ... in order on one stream and one workspace gives
+ * the same result as moe_layer_forward (phase -1 runs all of them). A phase reads what the
+ * previous phases left in the workspace. The launches are
+ *   decode (T <= 16, H <= 2048, F, Fs <= 512): router + shared expert; top-k + gate/up of the
+ *     selected experts; down projection + combine
+ *   other decode shapes: router; top-k + permutation; gate/up; down + combine
+ *   prefill: router; top-k; permutation; gate/up GEMM; down GEMM; combine
+ *     (MOE_FLAG_ATOMIC_COMBINE: ...; gate/up GEMM; zero fill of out; down GEMM + combine). */
+int32_t moe_layer_num_phases(const moe_layer_desc_t* desc, int32_t T, int32_t flags);
+int moe_layer_forward_phase(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T,
+                            float* out, void* workspace, size_t ws_bytes, int32_t flags,
+                            int32_t phase, void* stream);
+
+/* Residual update and RMSNorm between stacked layers ([P1] "The Model ...": a 40-layer stack;
+ * "How It Works ...": the next step's input stays in a GPU-resident slot):
+ *   init == 0: resid += y, then x = bf16( resid / sqrt(mean(resid^2) + eps) ) per row
+ *   init == 1: resid = x (bf16 widened to fp32), then x = bf16(RMSNorm(resid)); y unused
+ * y, resid [T, H] fp32, x [T, H] bf16 (read in place when init == 1), unit norm weight.
+ * H a multiple of 64, at most 16384; eps >= 0. */
+int moe_residual_rmsnorm(const float* y, float* resid, uint16_t* x, int32_t T, int32_t H,
+                         float eps, int32_t init, void* stream);
+
+/* A stack of MoE layers with the residual stream between them (pre-norm):
+ *   resid = x;  x = bf16(RMSNorm(resid));
+ *   for each layer l:  y = moe_layer_forward(layers[l], x);  resid += y;  x = bf16(RMSNorm(resid))
+ * On entry x [T, H] bf16 holds the tokens; on return resid [T, H] fp32 holds the final
+ * residual stream and x its normalised bf16 copy -- the input of the next decode step, left on
+ * the device. All layers must share `hidden`. workspace: moe_stack_workspace_bytes(...)
+ * (0 if invalid). Enqueue only, graph-capturable like moe_layer_forward. */
+size_t moe_stack_workspace_bytes(const moe_layer_desc_t* const* layers, int32_t n_layers,
+                                 int32_t T_max, int32_t flags);
+int moe_stack_forward(const moe_layer_desc_t* const* layers, int32_t n_layers, float* resid,
+                      uint16_t* x, int32_t T, float eps, void* workspace, size_t ws_bytes,
+                      int32_t flags, void* stream);
+
 /* Test export: dequantise row `row` of matrix `mat` of a projection with input size Kin
  * using the same device code as the GEMM kernels. out_f32 [Kin] receives scale*q + bias
  * as computed in fp32, out_bf16 [Kin] its bf16 rounding (either may be NULL). */

@@ -220,10 +220,47 @@ def layer_forward_per_token(layer: dict, x_bits, top_k: int, profile: str = "exa
 
 
 # ------------------------------------------------------------------- stack of layers
-def rms_norm(r, eps: float = 1e-6) -> np.ndarray:
+# The pages give the model's depth ([P1 "The Model ..."]: 10 full-attention and 30 Gated
+# DeltaNet layers, each with this MoE block) and keep the next step's input on the GPU
+# ([P1 "How It Works ..."]). The stacked workload is read as a pre-norm residual stream:
+#   r_0 = x,  x_l = bf16(RMSNorm(r_l)),  r_{l+1} = r_l + MoE_l(x_l)
+# with RMSNorm(r) = r / sqrt(mean(r^2) + eps), unit weight, eps = 1e-6.
+RMS_EPS = 1e-6
+
+
+def rms_norm(r, eps: float = RMS_EPS) -> np.ndarray:
     """r / sqrt(mean(r^2) + eps) with unit weight, per row."""
     r = np.asarray(r, dtype=np.float64)
     return r / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+
+
+def bf16_bits(values) -> np.ndarray:
+    """uint16 patterns of values that are exactly representable in bf16 (e.g. round_to_bf16
+    output); bf16 is the upper half of the fp32 pattern."""
+    v = np.asarray(values, dtype=np.float64).astype(np.float32)
+    u = v.view(np.uint32)
+    assert np.array_equal(v.astype(np.float64), np.asarray(values, dtype=np.float64)), "not bf16"
+    assert not np.any(u & np.uint32(0xFFFF)), "not bf16"
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def residual_rmsnorm(resid, y, eps: float = RMS_EPS):
+    """One step of the residual stream: r' = r + y (y may be None: r' = r), and the next
+    layer's input x' = bf16(RMSNorm(r')) as bf16 bit patterns. Returns (r', x' bits)."""
+    r = np.asarray(resid, dtype=np.float64)
+    if y is not None:
+        r = r + np.asarray(y, dtype=np.float64)
+    return r, bf16_bits(round_to_bf16(rms_norm(r, eps)))
+
+
+def stack_forward(layers, x_bits, top_k: int, profile: str = "bf16", eps: float = RMS_EPS):
+    """The whole stack for tokens x (bf16 bits): returns the final residual stream r_L and
+    x_L = bf16(RMSNorm(r_L)) (bits), following the recurrence above layer by layer."""
+    r, x = residual_rmsnorm(bf16_to_f64(x_bits), None, eps)
+    for layer in layers:
+        y = layer_forward(layer, x, top_k, profile)
+        r, x = residual_rmsnorm(r, y, eps)
+    return r, x
 
 
 # ---------------------------------------------------------------------- tolerances

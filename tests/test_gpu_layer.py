@@ -24,6 +24,7 @@ CASES = [
     ("mid", 1, 0), ("mid", 13, 0), ("mid", 13, FORCE), ("mid", 17, 0), ("mid", 300, 0),
     ("mid", 300, ATOMIC),
     ("full", 1, 0), ("full", 8, 0), ("full", 16, 0), ("full", 8, FORCE),
+    ("wide", 1, 0), ("wide", 4, 0), ("wide", 40, 0),
 ]
 
 

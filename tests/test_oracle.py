@@ -454,3 +454,48 @@ def test_generator_recipe():
     assert np.array_equal(L1["down"][0][17], L["down"][0][17])
     skew = synth.make_layer(synth.SHAPES["full_skew"], seed=0)["router_bias"]
     assert np.allclose(skew, -1.2 * np.log(np.arange(1, 257)), rtol=1e-6)
+
+
+# ------------------------------------------------------------------ stack glue
+def test_residual_rmsnorm_closed_forms():
+    # y = -r: the stream cancels and the normalised input is exactly zero (eps > 0)
+    r = np.array([[1.5, -2.0, 0.25, 8.0]])
+    r2, x = O.residual_rmsnorm(r, -r)
+    assert np.all(r2 == 0) and np.all(x == 0)
+    # a constant row c: x = c / sqrt(c^2 + eps), rounded to bf16 (hand value for c = 3)
+    c = 3.0
+    _, x = O.residual_rmsnorm(np.full((1, 64), c), None, eps=1e-6)
+    want = c / math.sqrt(c * c + 1e-6)            # 0.99999994..., rounds to 1.0 in bf16
+    assert np.all(O.bf16_to_f64(x) == 1.0) and abs(want - 1.0) < 2 ** -9
+    # with eps = 0 a power-of-two scaling of the row changes nothing at all
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal((2, 128))
+    _, xa = O.residual_rmsnorm(row, None, eps=0.0)
+    _, xb = O.residual_rmsnorm(row * 1024.0, None, eps=0.0)
+    assert np.array_equal(xa, xb)
+    # mean of squares of the normalised row is 1 before rounding (eps = 0)
+    assert abs(np.mean(O.rms_norm(row, 0.0) ** 2) - 1.0) < 1e-12
+
+
+def test_bf16_bits_round_trip():
+    bits = _all_finite_bf16()
+    assert np.array_equal(O.bf16_bits(O.bf16_to_f64(bits)), bits)
+    with pytest.raises(AssertionError):
+        O.bf16_bits(np.array([1.0 + 2 ** -10]))
+
+
+def test_stack_of_zero_layers_keeps_the_stream():
+    """Layers whose routed and shared weights are all zero output zero, so the residual stream
+    stays the input exactly and the final input is the normalised tokens."""
+    shape = synth.LayerShape(128, 4, 2, 64, 64)
+    layer = synth.make_layer(shape, seed=5)
+    for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        q, sc, b = layer[name]
+        layer[name] = (q, np.zeros_like(sc), np.zeros_like(b))
+    x = synth.make_tokens(shape, 3, seed=5)
+    r, xl = O.stack_forward([layer, layer], x, shape.K)
+    assert np.array_equal(r, O.bf16_to_f64(x))
+    # the hand-computed normalisation of token 0
+    row = O.bf16_to_f64(x[0])
+    want = O.round_to_bf16(row / math.sqrt(float(np.mean(row * row)) + 1e-6))
+    assert np.array_equal(O.bf16_to_f64(xl[0]), want)
