@@ -101,9 +101,13 @@ def _proj(seed, layer, expert, proj, n_out, k_in):
     return q, s_bits, b_bits
 
 
-def make_layer(shape: LayerShape, seed: int = 0, layer: int = 0) -> dict:
+def make_layer(shape: LayerShape, seed: int = 0, layer: int = 0, reuse: dict | None = None) -> dict:
     """Host arrays for one layer. Keys: router_w, router_bias (or None), shared_gate_w,
-    gate/up/down and sh_gate/sh_up/sh_down as (q, scale, bias) tuples."""
+    gate/up/down and sh_gate/sh_up/sh_down as (q, scale, bias) tuples.
+
+    `reuse`, a dict an earlier call returned for the same shape, has its routed-expert arrays
+    overwritten in place (the values are those of a fresh call); it spares the first-touch cost
+    of a new 450 MB allocation when many layers pass through host memory one at a time."""
     H, E, F, Fs = shape.H, shape.E, shape.F, shape.Fs
     assert H % GROUP == 0 and F % GROUP == 0 and Fs % GROUP == 0
     out = {}
@@ -112,9 +116,13 @@ def make_layer(shape: LayerShape, seed: int = 0, layer: int = 0) -> dict:
     out["shared_gate_w"] = _rng(seed, layer, _K_SGATE).normal(0.0, 0.02, size=(H,)).astype(np.float32)
 
     for name, pid, n_out, k_in in (("gate", _P_GATE, F, H), ("up", _P_UP, F, H), ("down", _P_DOWN, H, F)):
-        q = np.empty((E, n_out, k_in // 8), np.uint32)
-        s = np.empty((E, n_out, k_in // GROUP), np.uint16)
-        b = np.empty_like(s)
+        if reuse is not None:
+            q, s, b = reuse[name]
+            assert q.shape == (E, n_out, k_in // 8) and s.shape == (E, n_out, k_in // GROUP)
+        else:
+            q = np.empty((E, n_out, k_in // 8), np.uint32)
+            s = np.empty((E, n_out, k_in // GROUP), np.uint16)
+            b = np.empty_like(s)
         for e in range(E):
             q[e], s[e], b[e] = _proj(seed, layer, e, pid, n_out, k_in)
         out[name] = (q, s, b)
