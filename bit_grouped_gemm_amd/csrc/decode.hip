@@ -17,14 +17,14 @@
 //     with SwiGLU (one wave per row pair);
 //   B (k_dec_b): every workgroup selects each token's top-k from the logits (the same result in
 //     all of them), groups the (token, rank) slots by expert in LDS (stable grouped rows by
-//     counting), and its waves stream the selected experts' gate/up rows (a 1 KiB row per wave,
-//     16 bytes per lane), dequantise them in registers and store A = bf16(silu(G) * U);
-//     workgroup 0 also stores the per-expert route record for C;
+//     counting; a single token's experts are its ranks), and its waves stream the selected
+//     experts' gate/up rows (a 1 KiB row per wave, 16 bytes per lane), dequantise them in
+//     registers and store A = bf16(silu(G) * U); workgroup 0 also stores the per-expert route
+//     record for C;
 //   C (k_dec_c): down projection fused with the weighted combine. The route record and the
-//     activations are staged in LDS; a 32-lane half wave owns output row h, its two 16-lane
-//     groups walk the even and odd entries of the expert list (ascending expert id, then the
-//     shared expert) and add their two partial sums in a fixed order, so the result is
-//     deterministic.
+//     activations are staged in LDS; each 16-lane group owns output rows, the four waves of a
+//     workgroup walk interleaved quarters of the entry list (the shared expert last), and their
+//     partial sums are added in LDS in a fixed order, so the result is deterministic.
 // Every selected weight byte is read from HBM once per call.
 #include "moe_internal.h"
 
@@ -32,7 +32,7 @@ namespace moe {
 
 namespace {
 constexpr int kCH = 4;  // 16-byte chunks (32 inputs) per lane of a gate/up row (H <= 2048)
-constexpr int kNB = 8;  // down rows requested per batch by one 16-lane group
+constexpr int kNB = 4;  // down rows requested per batch by one 16-lane group
 }  // namespace
 
 struct DecodeArgs {
@@ -79,23 +79,24 @@ __device__ __forceinline__ void group_reduce(float (&v)[N], int r) {
 // 16-byte load per row and lane, a 1 KiB row per wave).
 struct PairW {
   uint4 g, u;
-  uint32_t gs, gb, us, ub;  // raw bf16 bits: converted when used, so a prefetch never waits
+  // raw bf16 bits, kept 16-bit so that the loaded value is the register itself (a widening at
+  // a loop-carried copy would make the wave wait for the load); converted when used
+  uint16_t gs, gb, us, ub;
 };
 
+// Every load is unconditional (lanes past the row re-read its last chunk, whose products are
+// never used): a load whose destination is merged with a value from another branch has to be
+// copied, and the copy makes the wave wait for the load right away.
 __device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe_w4_t& U,
                                           size_t row, int H, int lane) {
-  if (lane < (H >> 5)) {
-    const size_t sidx = row * (size_t)(H >> 6) + (lane >> 1);
-    w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[lane];
-    w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[lane];
-    w.gs = G.scale[sidx];
-    w.gb = G.bias[sidx];
-    w.us = U.scale[sidx];
-    w.ub = U.bias[sidx];
-  } else {
-    w.g = w.u = make_uint4(0, 0, 0, 0);
-    w.gs = w.gb = w.us = w.ub = 0u;
-  }
+  const int c = lane < (H >> 5) ? lane : (H >> 5) - 1;
+  const size_t sidx = row * (size_t)(H >> 6) + (c >> 1);
+  w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[c];
+  w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[c];
+  w.gs = G.scale[sidx];
+  w.gb = G.bias[sidx];
+  w.us = U.scale[sidx];
+  w.ub = U.bias[sidx];
 }
 
 // Partial gate and up dot products of the lane's chunk with the m tokens listed in tok (token
@@ -155,8 +156,8 @@ __device__ __forceinline__ void pair_finish(float (&v)[2 * TC], int lane, int m,
   if (lane % (2 * s) == 0 && j < m) a[a_row(j) + f] = f32_to_bf16(silu_mul(v[0], u));
 }
 
-// Routing of one call as per-expert entries, in LDS. Entry d (d < D, ascending expert id) is
-// expert ent_e[d] with ent_m[d] tokens, whose grouped rows start at ent_row0[d]; bit t of
+// Routing of one call as per-expert entries, in LDS. Entry d (d < D; ascending expert id, or
+// rank order for a single token) is expert ent_e[d] with ent_m[d] tokens, whose grouped rows start at ent_row0[d]; bit t of
 // ent_mask[d] is set if token t routes to it. Grouped row r belongs to token row_tok[r] with
 // routing weight row_w[r] (tokens ascending inside an expert). The words from `nd` through sgs
 // are also the route record that B hands to C.
@@ -247,7 +248,8 @@ template <int TC>
 __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint4 smem[];
   const int T = p.T, H = p.H, E = p.E, F = p.F, Fs = p.Fs, TK = T * p.K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int task = blockIdx.x * 4 + wave;
   const int nA = E + (Fs > 0 ? 1 + Fs : 0);
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [T, H]
@@ -327,7 +329,8 @@ template <int TC, int NJ>
 __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint4 smem[];
   const int T = p.T, H = p.H, E = p.E, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int NW = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [T, H]
   int* sel_idx = reinterpret_cast<int*>(xs + (size_t)T * H);        // [TK]
@@ -337,70 +340,125 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
   int* off = reinterpret_cast<int*>(tmask + E);                     // [E]
   const Route R = carve_route(off + E, TK, T);
 
-  // logits of this wave's first token requested before x is staged
+  // logits of this wave's first token and the shared-gate logits, requested before x is staged
+  // (the logits region always holds the T gate logits after the T x E router logits)
   float lv[NJ];
   if (wave < T) load_logits<NJ>(p.b.logits + (size_t)wave * E, E, lane, lv);
+  const float glog = p.b.logits[(size_t)T * E + (tid < T ? tid : T - 1)];
   stage_x(xs, p.x, (T * H) >> 3);
-  for (int e = tid; e < E; e += 256) {
-    cnt[e] = 0;
-    tmask[e] = 0u;
-  }
-  __syncthreads();
-  for (int t = wave; t < T; t += 4) {
-    if (t != wave) load_logits<NJ>(p.b.logits + (size_t)t * E, E, lane, lv);
-    float my_v, my_w;
-    int my_i;
-    wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w);
-    if (lane < K) {
-      sel_idx[t * K + lane] = my_i;
-      sel_w[t * K + lane] = my_w;
-      atomicAdd(&cnt[my_i], 1);
-      atomicOr(&tmask[my_i], 1u << t);
+  if (T > 1)
+    for (int e = tid; e < E; e += 256) {
+      cnt[e] = 0;
+      tmask[e] = 0u;
     }
-    if (lane == 0 && Fs > 0) R.sgs[t] = 1.0f / (1.0f + __expf(-p.b.logits[(size_t)T * E + t]));
-  }
+  if (tid < T && Fs > 0) R.sgs[tid] = 1.0f / (1.0f + __expf(-glog));
   __syncthreads();
-  build_route(R, sel_idx, sel_w, cnt, tmask, off, T, E, K);
+  if (T == 1) {
+    // one token: its K experts are distinct, so the entries are the ranks themselves (entry k =
+    // the rank-k expert, one row, A row k); no grouping pass is needed
+    if (wave == 0) {
+      float my_v, my_w;
+      int my_i;
+      wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w);
+      if (lane < K) {
+        R.ent_e[lane] = my_i;
+        R.ent_m[lane] = 1;
+        R.ent_row0[lane] = lane;
+        R.ent_mask[lane] = 1u;
+        R.row_w[lane] = my_w;
+        R.row_tok[lane] = 0;
+      }
+      if (lane == 0) *R.nd = K;
+    }
+    __syncthreads();
+  } else {
+    for (int t = wave; t < T; t += 4) {
+      if (t != wave) load_logits<NJ>(p.b.logits + (size_t)t * E, E, lane, lv);
+      float my_v, my_w;
+      int my_i;
+      wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w);
+      if (lane < K) {
+        sel_idx[t * K + lane] = my_i;
+        sel_w[t * K + lane] = my_w;
+        atomicAdd(&cnt[my_i], 1);
+        atomicOr(&tmask[my_i], 1u << t);
+      }
+    }
+    __syncthreads();
+    build_route(R, sel_idx, sel_w, cnt, tmask, off, T, E, K);
+  }
   if (blockIdx.x == 0) {  // the route record for the down projection
     const int n = (int)route_words(TK, T);
     for (int i = tid; i < n; i += 256) p.b.route[i] = R.nd[i];
   }
   const int D = *R.nd;
 
+  // Tasks task = gw + NW*i, in batches of kPB; the next batch's rows are requested before the
+  // current batch is used. Indices past the last task are clamped to it (wasted loads of one
+  // row, never used), so no load is conditional.
   const int nB = D * F;
-  PairW wc, wn;
-  int task = gw;
-  if (task < nB) load_pair(wc, p.gate, p.up, (size_t)R.ent_e[task / F] * F + task % F, H, lane);
-  for (; task < nB; task += NW) {
-    const int nxt = task + NW;
-    if (nxt < nB) load_pair(wn, p.gate, p.up, (size_t)R.ent_e[nxt / F] * F + nxt % F, H, lane);
-    const int d = task / F, f = task % F;
-    const int m = R.ent_m[d], row0 = R.ent_row0[d];
-    float v[2 * TC];
-    pair_dots<TC>(wc, xs, H, lane, R.row_tok + row0, m, v);
-    pair_finish<TC>(v, lane, m, f, p.b.a, [&](int j) { return (size_t)(row0 + j) * F; });
-    if (nxt < nB) wc = wn;
+  constexpr int kPB = 2;
+  const int step = kPB * NW;
+  auto issue = [&](PairW (&w)[kPB], int t0) {
+#pragma unroll
+    for (int b = 0; b < kPB; ++b) {
+      int tk = t0 + b * NW;
+      tk = tk < nB ? tk : nB - 1;
+      load_pair(w[b], p.gate, p.up, (size_t)R.ent_e[tk / F] * F + tk % F, H, lane);
+    }
+  };
+  auto run = [&](const PairW (&w)[kPB], int t0) {
+#pragma unroll
+    for (int b = 0; b < kPB; ++b) {
+      const int tk = t0 + b * NW;
+      if (tk < nB) {  // uniform over the wave
+        const int d = tk / F, f = tk % F;
+        const int m = R.ent_m[d], row0 = R.ent_row0[d];
+        float v[2 * TC];
+        pair_dots<TC>(w[b], xs, H, lane, R.row_tok + row0, m, v);
+        pair_finish<TC>(v, lane, m, f, p.b.a, [&](int j) { return (size_t)(row0 + j) * F; });
+      }
+    }
+  };
+  PairW w0[kPB], w1[kPB];
+  int t0 = gw;
+  if (t0 < nB) issue(w0, t0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (; t0 < nB; t0 += 2 * step) {
+    if (t0 + step < nB) issue(w1, t0 + step);
+    __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the use of w0
+    run(w0, t0);
+    if (t0 + step >= nB) break;
+    if (t0 + 2 * step < nB) issue(w0, t0 + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
+    run(w1, t0 + step);
   }
 }
 
 // ============================================================================ C
 struct DownW {
   uint4 q;
-  uint32_t s, b;  // raw bf16 bits
+  uint16_t s, b;  // raw bf16 bits (16-bit for the same reason as in PairW)
 };
 
+// A workgroup owns 4*HG consecutive output rows: 16-lane group g of every wave takes rows
+// h = 4*(HG*blockIdx.x + r) + g, r < HG. Wave w walks the entries d = w, w + 4, ... (ascending
+// expert id, the shared expert last), so the four groups of a wave read the same activation
+// chunks. Each lane sl of a group accumulates the weighted sum for token sl; the four waves'
+// sums are added in LDS in a fixed order, so the result is deterministic.
 // A_LDS: the activations of the call are staged in LDS (when they fit) instead of being read
 // from global memory for every entry.
-template <int TC, bool A_LDS>
+template <int TC, int HG, bool A_LDS>
 __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint4 smem[];
   const int T = p.T, H = p.H, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int sl = lane & 15, grp = lane >> 4;
-  const int NW = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
   const size_t a_elems = (size_t)TK * F + (size_t)T * Fs;
   uint16_t* as = reinterpret_cast<uint16_t*>(smem);                       // [a_elems] if A_LDS
-  const Route R = carve_route(A_LDS ? (void*)(as + a_elems) : (void*)smem, TK, T);
+  float* part = reinterpret_cast<float*>(A_LDS ? (void*)(as + a_elems) : (void*)smem);
+  const Route R = carve_route(part + 4 * HG * 64, TK, T);                 // part: [4][HG][64]
 
   const int nw = (int)route_words(TK, T);
   for (int i = tid; i < nw; i += 256) R.nd[i] = p.b.route[i];
@@ -410,86 +468,118 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
   __syncthreads();
   const int D = *R.nd;
   const int nD = D + (Fs > 0 ? 1 : 0);  // the shared expert is the last entry
+  const int ni = wave < nD ? (nD - wave + 3) >> 2 : 0;  // entries of this wave
   const uint16_t* abase = A_LDS ? as : p.b.a;
 
-  const int q2 = grp & 1;  // this group takes the entries d = q2, q2 + 2, ...
-  auto load_down = [&](int h, int dfirst, DownW (&dw)[kNB]) {
+  // Entries i0 .. i0+kNB-1 of this wave for row h. Entries past the wave's list are clamped to
+  // the last entry and lanes past a short row re-read its last chunk (both never used), so every
+  // load is unconditional; the weight pointers are selected as values, not as references into
+  // the argument block (which would be read with vector loads and waited for).
+  const uint32_t* const rq = p.down.q;
+  const uint16_t* const rs = p.down.scale;
+  const uint16_t* const rb = p.down.bias;
+  const uint32_t* const sq = p.sh_down.q;
+  const uint16_t* const ss = p.sh_down.scale;
+  const uint16_t* const sb = p.sh_down.bias;
+  auto load_down = [&](int h, int i0, DownW (&dw)[kNB]) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const int d = dfirst + 2 * b;
-      dw[b].q = make_uint4(0, 0, 0, 0);
-      dw[b].s = dw[b].b = 0u;
-      if (d < nD) {
-        const bool sh = d == D;
-        const int Kd = sh ? Fs : F;
-        if (sl < (Kd >> 5)) {
-          const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
-          const moe_w4_t& W = sh ? p.sh_down : p.down;
-          dw[b].q = reinterpret_cast<const uint4*>(W.q + row * (size_t)(Kd >> 3))[sl];
-          dw[b].s = W.scale[row * (size_t)(Kd >> 6) + (sl >> 1)];
-          dw[b].b = W.bias[row * (size_t)(Kd >> 6) + (sl >> 1)];
+      int d = wave + 4 * (i0 + b);
+      d = d < nD ? d : nD - 1;
+      const bool sh = d == D;
+      const int Kd = sh ? Fs : F;
+      const int c = sl < (Kd >> 5) ? sl : (Kd >> 5) - 1;
+      const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
+      const uint32_t* q = sh ? sq : rq;
+      const uint16_t* sp = sh ? ss : rs;
+      const uint16_t* bp = sh ? sb : rb;
+      const size_t g = row * (size_t)(Kd >> 6) + (c >> 1);
+      dw[b].q = reinterpret_cast<const uint4*>(q + row * (size_t)(Kd >> 3))[c];
+      dw[b].s = sp[g];
+      dw[b].b = bp[g];
+    }
+  };
+  auto use_down = [&](int i0, const DownW (&dw)[kNB], float& acc) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      if (i0 + b >= ni) break;  // uniform over the wave
+      const int d = wave + 4 * (i0 + b);
+      const bool sh = d == D;
+      const int Kd = sh ? Fs : F;
+      const int m = sh ? T : R.ent_m[d];
+      const int row0 = sh ? 0 : R.ent_row0[d];
+      const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
+      uint32_t wd[16];
+      const float ds = bf16_to_f32(dw[b].s), db = bf16_to_f32(dw[b].b);
+      dequant8(dw[b].q.x, ds, db, wd + 0);
+      dequant8(dw[b].q.y, ds, db, wd + 4);
+      dequant8(dw[b].q.z, ds, db, wd + 8);
+      dequant8(dw[b].q.w, ds, db, wd + 12);
+      float dots[TC];
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        dots[j] = 0.0f;
+        if (j < m && sl < (Kd >> 5)) {
+          const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
+                                  : abase + (size_t)(row0 + j) * F;
+          const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
+          float s = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 a4 = av[q];
+            s = dot2_bf16(a4.x, wd[4 * q + 0], s);
+            s = dot2_bf16(a4.y, wd[4 * q + 1], s);
+            s = dot2_bf16(a4.z, wd[4 * q + 2], s);
+            s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+          }
+          dots[j] = s;
         }
       }
+      group_reduce<TC, 16>(dots, sl);
+      // lane sl (= token) takes its entry: the token's rank inside this expert
+      int j = 0;
+      bool mine = false;
+      float wgt = 0.0f;
+      if (sl < T && ((tmask >> sl) & 1u)) {
+        j = __popc(tmask & ((1u << sl) - 1u));
+        mine = true;
+        wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
+      }
+      const float val = TC == 1 ? dots[0] : __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
+      if (mine) acc = __builtin_fmaf(wgt, val, acc);
     }
   };
 
-  for (int hp = gw; 2 * hp < H; hp += NW) {
-    const int h = 2 * hp + (lane >> 5);
+  // batches of kNB entries, the next batch requested before the current one is used
+#pragma unroll
+  for (int r = 0; r < HG; ++r) {
+    const int h = 4 * (HG * (int)blockIdx.x + r) + grp;
     float acc = 0.0f;
-    DownW dw[kNB];
-    for (int d0 = q2; d0 < nD; d0 += 2 * kNB) {
-      load_down(h, d0, dw);
-#pragma unroll
-      for (int b = 0; b < kNB; ++b) {
-        const int d = d0 + 2 * b;
-        if (d >= nD) break;  // uniform across the 16-lane group
-        const bool sh = d == D;
-        const int Kd = sh ? Fs : F;
-        const int m = sh ? T : R.ent_m[d];
-        const int row0 = sh ? 0 : R.ent_row0[d];
-        const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
-        uint32_t wd[16];
-        const float ds = bf16_to_f32(dw[b].s), db = bf16_to_f32(dw[b].b);
-        dequant8(dw[b].q.x, ds, db, wd + 0);
-        dequant8(dw[b].q.y, ds, db, wd + 4);
-        dequant8(dw[b].q.z, ds, db, wd + 8);
-        dequant8(dw[b].q.w, ds, db, wd + 12);
-        float dots[TC];
-#pragma unroll
-        for (int j = 0; j < TC; ++j) {
-          dots[j] = 0.0f;
-          if (j < m && sl < (Kd >> 5)) {
-            const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
-                                    : abase + (size_t)(row0 + j) * F;
-            const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
-            float s = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint4 a4 = av[q];
-              s = dot2_bf16(a4.x, wd[4 * q + 0], s);
-              s = dot2_bf16(a4.y, wd[4 * q + 1], s);
-              s = dot2_bf16(a4.z, wd[4 * q + 2], s);
-              s = dot2_bf16(a4.w, wd[4 * q + 3], s);
-            }
-            dots[j] = s;
-          }
-        }
-        group_reduce<TC, 16>(dots, sl);
-        // lane sl (= token) takes its entry: the token's rank inside this expert
-        int j = 0;
-        bool mine = false;
-        float wgt = 0.0f;
-        if (sl < T && ((tmask >> sl) & 1u)) {
-          j = __popc(tmask & ((1u << sl) - 1u));
-          mine = true;
-          wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
-        }
-        const float val = TC == 1 ? dots[0] : __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
-        if (mine) acc = __builtin_fmaf(wgt, val, acc);
+    if (ni > 0) {
+      DownW w0[kNB], w1[kNB];
+      load_down(h, 0, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int i0 = 0; i0 < ni; i0 += 2 * kNB) {
+        if (i0 + kNB < ni) load_down(h, i0 + kNB, w1);
+        __builtin_amdgcn_sched_barrier(0);
+        use_down(i0, w0, acc);
+        if (i0 + kNB >= ni) break;
+        if (i0 + 2 * kNB < ni) load_down(h, i0 + 2 * kNB, w0);
+        __builtin_amdgcn_sched_barrier(0);
+        use_down(i0 + kNB, w1, acc);
       }
     }
-    acc += __shfl_xor(acc, 16, 64);
-    if (q2 == 0 && sl < T) p.out[(size_t)sl * H + h] = acc;
+    part[(wave * HG + r) * 64 + lane] = acc;
+  }
+  __syncthreads();
+  // wave w writes rows r = w, w + 4, ... of the workgroup's HG row sets
+  for (int r = wave; r < HG; r += 4) {
+    const int h = 4 * (HG * (int)blockIdx.x + r) + grp;
+    if (sl < T) {
+      const float v = ((part[(0 * HG + r) * 64 + lane] + part[(1 * HG + r) * 64 + lane]) +
+                       part[(2 * HG + r) * 64 + lane]) + part[(3 * HG + r) * 64 + lane];
+      p.out[(size_t)sl * H + h] = v;
+    }
   }
 }
 
@@ -547,11 +637,12 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const size_t lds_x = (size_t)d.T * d.H * 2;
   const size_t lds_b = lds_x + decode_b_lds_words(d) * 4;
   const size_t a_bytes = ((size_t)d.TK() * d.F + (size_t)d.T * d.Fs) * 2;
-  const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4;
+  const int HG = d.T <= 2 ? 1 : 2;  // output rows per 16-lane group
+  const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4 + (size_t)4 * HG * 64 * 4;
   const bool a_lds = a_bytes + lds_c_route <= kDecLdsMax;
   const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
   const int nA = d.E + (d.Fs > 0 ? 1 + d.Fs : 0);
-  const dim3 gA((nA + 3) / 4), gB(2 * device_cus()), gC((d.H / 2 + 3) / 4), blk(256);
+  const dim3 gA((nA + 3) / 4), gB(4 * device_cus()), gC(d.H / (4 * HG)), blk(256);
 #define MOE_DEC(TCV, NJV)                                                        \
   do {                                                                           \
     if (phase < 0 || phase == 0)                                                 \
@@ -559,10 +650,11 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
     if (phase < 0 || phase == 1)                                                 \
       hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);             \
     if (phase < 0 || phase == 2) {                                               \
+      constexpr int HGV = TCV <= 2 ? 1 : 2;                                      \
       if (a_lds)                                                                 \
-        hipLaunchKernelGGL((k_dec_c<TCV, true>), gC, blk, lds_c, s, p);          \
+        hipLaunchKernelGGL((k_dec_c<TCV, HGV, true>), gC, blk, lds_c, s, p);     \
       else                                                                       \
-        hipLaunchKernelGGL((k_dec_c<TCV, false>), gC, blk, lds_c, s, p);         \
+        hipLaunchKernelGGL((k_dec_c<TCV, HGV, false>), gC, blk, lds_c, s, p);    \
     }                                                                            \
   } while (0)
 #define MOE_DEC_T(NJV) \

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 #include "moe_w4.h"
@@ -183,69 +184,82 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
-// Maximum of v over the wave, returned to every lane. Rows of 16 lanes reduce with DPP row
-// shifts (no LDS round trip); the four row maxima are read from lanes 15, 31, 47, 63.
-__device__ __forceinline__ float wave_max(float v) {
-  const int ninf = __float_as_int(-INFINITY);
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xF, 0xF, false)));
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+// Maximum of v over the wave, returned to every lane (as a scalar). DPP row shifts 1, 2, 4, 8
+// leave each row's maximum in its lane 15; row_bcast:15 and row_bcast:31 then carry it into
+// lane 63, which is read once. Lanes with no DPP source take INT_MIN (the identity).
+__device__ __forceinline__ int wave_max_i32(int v) {
+  constexpr int kMin = INT_MIN;
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(kMin, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// fp32 -> int32 key with the same order (for non-NaN values): negative values have their
+// magnitude bits inverted. -0 is first turned into +0 (x + 0 = +0 for x = -0), so that equal
+// values have equal keys. INT_MIN lies below every key of a non-NaN value (-inf included).
+__device__ __forceinline__ int order_key(float x) {
+  const int b = __float_as_int(x + 0.0f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_value(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 
 // Top-k of one token's E logits by one wave (E <= 64*NJ) with the softmax over the selected
-// logits. Lane l holds logits e = l + 64*j in v[j]. Each of the K rounds takes the wave maximum
-// M of the remaining logits; the winner is the lowest expert index whose logit equals M (one
-// ballot per j: for fixed j the lanes are in expert order, and j-blocks ascend). Lane r < K ends
-// with the rank-r expert my_i, its logit my_v and its renormalised weight
-// my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank order; lanes >= K get
-// my_w = 0.
+// logits. Lane l holds logits e = NJ*l + j in v[j] (consecutive experts per lane). Each of the
+// K rounds takes the wave maximum M of the remaining order keys; the winner is the lowest
+// expert index whose key equals M: the lowest lane holding one (one ballot), then the lowest
+// j in that lane. Lane r < K ends with the rank-r expert my_i, its logit my_v and its
+// renormalised weight my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank
+// order; lanes >= K get my_w = 0.
 template <int NJ>
 __device__ __forceinline__ void wave_topk_softmax(const float (&v)[NJ], int E, int K, int lane,
                                                   float& my_v, int& my_i, float& my_w) {
-  uint32_t avail = 0;
+  int key[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    if (lane + 64 * j < E) avail |= 1u << j;
+  for (int j = 0; j < NJ; ++j) key[j] = NJ * lane + j < E ? order_key(v[j]) : INT_MIN;
   my_v = -INFINITY;
   my_i = 0;
   float my_z = 0.0f, m0 = 0.0f, den = 0.0f;
   for (int r = 0; r < K; ++r) {
-    float lm = -INFINITY;
+    int lm = key[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) lm = max(lm, key[j]);
+    const int M = wave_max_i32(lm);
+    int jf = NJ;  // first j of this lane holding M
+#pragma unroll
+    for (int j = NJ - 1; j >= 0; --j)
+      if (key[j] == M) jf = j;
+    const uint64_t b = __ballot(jf < NJ);
+    const int L = (int)__builtin_ctzll(b);
+    const int jL = __builtin_amdgcn_readlane(jf, L);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      if ((avail >> j) & 1u) lm = fmaxf(lm, v[j]);
-    const float M = wave_max(lm);
-    int win = -1;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint64_t b = __ballot(((avail >> j) & 1u) && v[j] == M);
-      if (win < 0 && b != 0) win = (int)__builtin_ctzll(b) + 64 * j;
-    }
-    if ((win & 63) == lane) avail &= ~(1u << (win >> 6));
-    if (r == 0) m0 = M;
-    const float z = __expf(M - m0);
+      if (lane == L && j == jL) key[j] = INT_MIN;
+    const float Mf = key_value(M);
+    if (r == 0) m0 = Mf;
+    const float z = __expf(Mf - m0);
     den += z;
     if (lane == r) {
-      my_v = M;
-      my_i = win;
+      my_v = Mf;
+      my_i = NJ * L + jL;
       my_z = z;
     }
   }
   my_w = lane < K ? my_z / den : 0.0f;
 }
 
+// Lane l takes logits NJ*l .. NJ*l + NJ - 1 (-inf past E).
 template <int NJ>
 __device__ __forceinline__ void load_logits(const float* __restrict__ lt, int E, int lane,
                                             float (&v)[NJ]) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
+    const int e = NJ * lane + j;
     v[j] = e < E ? lt[e] : -INFINITY;
   }
 }
