@@ -148,8 +148,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// silu(g) * u = g / (1 + e^-g) * u, with the hardware reciprocal (about 1 ulp) in place of
+// a full-precision division: the result is rounded to bf16 right after.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

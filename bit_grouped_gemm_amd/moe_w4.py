@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4.so")
 
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_WORKSPACE_TOO_SMALL, MOE_HIP_ERROR = range(5)
-MOE_BLOCK_M = 128
+MOE_BLOCK_M = 256
 MOE_GEMM_GATE_UP, MOE_GEMM_DOWN, MOE_GEMM_DOWN_COMBINE, MOE_GEMM_DOWN_COMBINE_ATOMIC = range(4)
 MOE_FLAG_ATOMIC_COMBINE = 1
 MOE_FLAG_FORCE_PREFILL = 2

@@ -109,7 +109,7 @@ typedef struct {
   int32_t* num_blocks;
 } moe_plan_t;
 
-#define MOE_BLOCK_M 128
+#define MOE_BLOCK_M 256
 
 /* moe_grouped_gemm_w4 `which` */
 enum {
