@@ -111,14 +111,16 @@ bool use_decode(const Dims& d, int flags) {
 int run_route(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, int32_t* idx,
               float* w, float* sgate, void* ws, const Layout& L, bool decode, hipStream_t s) {
   float* logits = at<float>(ws, L.logits);
+  const float* wg = d.Fs > 0 ? desc->shared_gate_w : nullptr;
   hipError_t e;
   if (decode) {
     e = launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
-  } else {
-    e = launch_router_logits_mfma(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
+  } else {  // the MFMA router forms the shared gate itself
+    e = launch_router_logits_mfma(x, desc->router_w, desc->router_bias, wg, d.T, d.E, d.H, logits,
+                                  sgate, s);
+    wg = nullptr;
   }
   if (e != hipSuccess) return MOE_HIP_ERROR;
-  const float* wg = d.Fs > 0 ? desc->shared_gate_w : nullptr;
   return hip_status(launch_topk(logits, x, wg, d.T, d.E, d.K, d.H, idx, w, sgate, s));
 }
 
@@ -204,9 +206,9 @@ int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* 
     step([&] { return launch_dec_gateup(d, *desc, x, plan, mb, a, s); });
     step([&] { return launch_dec_down(d, *desc, a, plan, w, sgate, out, s); });
   } else {
-    step([&] { return launch_router_logits_mfma(x, desc->router_w, desc->router_bias, d.T, d.E,
-                                                d.H, logits, s); });
-    step([&] { return launch_topk(logits, x, wg, d.T, d.E, d.K, d.H, idx, w, sgate, s); });
+    step([&] { return launch_router_logits_mfma(x, desc->router_w, desc->router_bias, wg, d.T,
+                                                d.E, d.H, logits, sgate, s); });
+    step([&] { return launch_topk(logits, x, nullptr, d.T, d.E, d.K, d.H, idx, w, sgate, s); });
     step([&] { return launch_permute(idx, d, d.Fs > 0, at<int32_t>(ws, L.hist), plan, s); });
     step([&] {
       const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);

@@ -41,8 +41,10 @@ struct GemmParams {
 enum GemmMode { kGateUp = 0, kDownStore = 1, kDownAtomic = 2 };
 
 // Launchers (return the launch status).
-hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias, int T,
-                                     int E, int H, float* logits, hipStream_t s);
+// wg != nullptr: also writes sgate[t] = sigmoid(x_t . wg).
+hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias,
+                                     const float* wg, int T, int E, int H, float* logits,
+                                     float* sgate, hipStream_t s);
 hipError_t launch_router_logits_gemv(const uint16_t* x, const float* w, const float* bias, int T,
                                      int E, int H, float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, const uint16_t* x, const float* wg, int T, int E,

@@ -67,12 +67,25 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   __shared__ int wave_tot[16];
   __shared__ int total_slots, total_blocks, bad;
   const int e = threadIdx.x;
+  // the rows are read eight at a time, so the latency of a row read is paid once per eight rows
   int cnt = 0;
   if (e < E)
-    for (int c = 0; c < nchunks; ++c) cnt += hist[(size_t)c * (E + 1) + e];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * (E + 1) + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cnt += v[i];
+    }
   if (threadIdx.x == 0) {
     int b = 0;
-    for (int c = 0; c < nchunks; ++c) b += hist[(size_t)c * (E + 1) + E];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * (E + 1) + E] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b += v[i];
+    }
     bad = b;
   }
   const int off = block_exclusive_scan_1024(e < E ? cnt : 0, wave_tot, &total_slots);
@@ -80,11 +93,16 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
     counts[e] = cnt;
     offsets[e] = off;
     int run = off;
-    for (int c = 0; c < nchunks; ++c) {
-      int32_t* p = hist + (size_t)c * (E + 1) + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * (E + 1) + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (c0 + i < nchunks) {
+          hist[(size_t)(c0 + i) * (E + 1) + e] = run;
+          run += v[i];
+        }
     }
   }
   const int nb = (e < E) ? (cnt + kBlockM - 1) / kBlockM : 0;
@@ -104,22 +122,47 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   if (threadIdx.x == 0) *num_blocks = bad ? -1 : total_blocks + nbs;
 }
 
-// One wave per chunk. For 64 slots at a time, the lanes that hold the same expert are found
-// with one ballot per bit of the expert id; a lane's rank among its peers is the number of
-// lower peer lanes, and the lowest peer advances the expert's running position afterwards.
-__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ idx, int TK, int E,
-                                                int nbits, const int32_t* __restrict__ base,
-                                                int32_t* __restrict__ sorted_slots,
-                                                int32_t* __restrict__ slot_pos) {
-  __shared__ int cur[1024];
-  const int lane = threadIdx.x;
-  const int32_t* row = base + (size_t)blockIdx.x * (E + 1);
-  for (int e = lane; e < E; e += 64) cur[e] = row[e];
+// One workgroup of 4 waves per chunk; wave w takes the w-th quarter of the chunk's slots.
+// Each wave first counts its quarter per expert; the counts of the lower quarters, added to
+// the chunk's starting positions, give each wave its own running positions, so the quarters
+// are scattered concurrently and the result is still stable. For 64 slots at a time, the
+// lanes that hold the same expert are found with one ballot per bit of the expert id; a
+// lane's rank among its peers is the number of lower peer lanes, and the lowest peer advances
+// the expert's running position afterwards.
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int TK, int E,
+                                                 int nbits, const int32_t* __restrict__ base,
+                                                 int32_t* __restrict__ sorted_slots,
+                                                 int32_t* __restrict__ slot_pos) {
+  __shared__ int cur[4][1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int e = tid; e < 4 * 1024; e += 256) (&cur[0][0])[e] = 0;
   __syncthreads();
   const int s0 = blockIdx.x * kChunkSlots, s1 = min(TK, s0 + kChunkSlots);
-  for (int sb = s0; sb < s1; sb += 64) {
+  constexpr int kQ = kChunkSlots / 4;
+  const int q0 = s0 + wave * kQ, q1 = min(s1, q0 + kQ);
+  // per-quarter counts (the quarter itself is the wave's own)
+  for (int s = q0 + lane; s < q1; s += 64) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cur[wave][e], 1);
+  }
+  __syncthreads();
+  // cur[w][e] <- chunk start of e + counts of e in quarters < w
+  const int32_t* row = base + (size_t)blockIdx.x * (E + 1);
+  for (int e = tid; e < E; e += 256) {
+    int run = row[e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = cur[w][e];
+      cur[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int* my = cur[wave];
+  for (int sb = q0; sb < q1; sb += 64) {
     const int s = sb + lane;
-    const int e = (s < s1) ? idx[s] : -1;
+    const int e = (s < q1) ? idx[s] : -1;
     const bool ok = e >= 0 && e < E;
     uint64_t peers = __ballot(ok);
     for (int b = 0; b < nbits; ++b) {
@@ -129,10 +172,10 @@ __global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ idx,
     }
     const uint64_t lower = peers & ((1ull << lane) - 1ull);
     int p = 0;
-    if (ok) p = cur[e] + __popcll(lower);
-    __syncthreads();
-    if (ok && lower == 0) cur[e] += __popcll(peers);
-    __syncthreads();
+    if (ok) p = my[e] + __popcll(lower);
+    // the wave's own LDS accesses complete in order: every lane's read of my[e] above comes
+    // before the lowest peer's update below
+    if (ok && lower == 0) my[e] += __popcll(peers);
     if (ok) {
       sorted_slots[p] = s;
       slot_pos[s] = p;
@@ -230,7 +273,7 @@ hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nchunks, d.E, d.T, d.K,
                      shared ? 1 : 0, plan.counts, plan.offsets,
                      reinterpret_cast<int4*>(plan.blocks), plan.num_blocks);
-  hipLaunchKernelGGL(k_scatter, dim3(nchunks), dim3(64), 0, s, idx, TK, d.E, nbits, hist,
+  hipLaunchKernelGGL(k_scatter, dim3(nchunks), dim3(256), 0, s, idx, TK, d.E, nbits, hist,
                      plan.sorted_slots, plan.slot_pos);
   return hipGetLastError();
 }

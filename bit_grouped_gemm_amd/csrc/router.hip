@@ -21,9 +21,17 @@ namespace moe {
 // to 144 B). Lane l feeds row (l & 31) of its tile and inputs 8*(l >> 5) .. +7 of the 16-input
 // step for both operands (any consistent split of K between the operands gives the same dot
 // products). Per step the low, middle and high parts are accumulated in that order.
+//
+// The global loads run two chunks ahead of the MFMAs (two register sets), and the barrier
+// between chunks waits only for the LDS stores, so the prefetch stays in flight across it.
+// Workgroups are dispatched round-robin over the 8 XCDs; XCD i takes a contiguous range of
+// tiles, so the expert tiles of one token tile read x through the same L2.
+// The workgroups of the first expert tile also form the shared-expert gate logit x . wg in fp32
+// from the x chunks they hold in LDS.
 namespace {
 constexpr int kRK = 64;        // inputs per K-chunk
 constexpr int kRRow = kRK + 8; // padded LDS row (bf16 elements)
+constexpr int kXcds = 8;
 }  // namespace
 
 // (v0, v1) -> three packed bf16 pairs whose sums are exact splits of v0 and v1.
@@ -38,61 +46,76 @@ __device__ __forceinline__ void split3(float v0, float v1, uint32_t& hi, uint32_
 
 __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ w,
-                                                        const float* __restrict__ bias, int T,
-                                                        int E, int H, float* __restrict__ logits) {
+                                                        const float* __restrict__ bias,
+                                                        const float* __restrict__ wg, int T,
+                                                        int E, int H, int n_etiles, int ntiles,
+                                                        float* __restrict__ logits,
+                                                        float* __restrict__ sgate) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * kRRow];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][64 * kRRow];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  __shared__ __attribute__((aligned(16))) float Gs[2][kRK];
+  const int per = gridDim.x / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= ntiles) return;  // whole workgroup, before any barrier
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = (tile / n_etiles) * 64, e0 = (tile % n_etiles) * 64;
+  const bool gate = wg != nullptr && e0 == 0;
+  const float* wgp = wg != nullptr ? wg : w;  // loads stay unconditional; unused without a gate
+  const int nchunks = H / kRK;
 
-  // staging: A = 64 rows x 8 segments of 8 bf16 (2 per thread), B = 64 rows x 16 float4 (4)
-  uint4 ar[2];
-  float4 br[4];
-  auto load = [&](int c) {
-    const int k0 = c * kRK;
+  // one chunk's registers: x (64 rows x 8 segments of 8 bf16, two per thread), router rows
+  // (64 rows x 16 float4, four per thread) and the shared gate weight k0 + (tid & 63)
+  auto load = [&](bf16x8_t (&ra)[2], float4 (&rb)[4], float& rg, int c) {
+    const int k0 = min(c, nchunks - 1) * kRK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + 256 * i, row = v >> 3, seg = v & 7;
       const int t = min(t0 + row, T - 1);
-      ar[i] = *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + seg * 8);
+      ra[i] = *reinterpret_cast<const bf16x8_t*>(x + (size_t)t * H + k0 + seg * 8);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = tid + 256 * i, row = v >> 4, c4 = v & 15;
       const int e = min(e0 + row, E - 1);
-      br[i] = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + c4 * 4);
+      rb[i] = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + c4 * 4);
     }
+    rg = wgp[k0 + lane];
   };
-  auto store = [&](int buf) {
+  auto store = [&](const bf16x8_t (&ra)[2], const float4 (&rb)[4], float rg, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + 256 * i, row = v >> 3, seg = v & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row * kRRow + seg * 8]) = ar[i];
+      *reinterpret_cast<bf16x8_t*>(&As[buf][row * kRRow + seg * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = tid + 256 * i, row = v >> 4, c4 = v & 15;
       uint2 h, m, l;
-      split3(br[i].x, br[i].y, h.x, m.x, l.x);
-      split3(br[i].z, br[i].w, h.y, m.y, l.y);
+      split3(rb[i].x, rb[i].y, h.x, m.x, l.x);
+      split3(rb[i].z, rb[i].w, h.y, m.y, l.y);
       const int o = row * kRRow + c4 * 4;
       *reinterpret_cast<uint2*>(&Bs[buf][0][o]) = h;
       *reinterpret_cast<uint2*>(&Bs[buf][1][o]) = m;
       *reinterpret_cast<uint2*>(&Bs[buf][2][o]) = l;
     }
+    if (wave == 0) Gs[buf][lane] = rg;
+  };
+  // LDS stores of this wave are complete, then the workgroup meets; outstanding global loads
+  // (the prefetch) are not waited for: vmcnt 63 in bits 3:0 and 15:14, expcnt 7, lgkmcnt 0.
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   const int r = lane & 31, half = lane >> 5;
   const int arow = (wave >> 1) * 32 + r, brow = (wave & 1) * 32 + r;
+  const int grow = tid >> 2, gq = tid & 3;  // gate: token row, quarter of the chunk
   f32x16_t acc = {};
-  const int nchunks = H / kRK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) load(c + 1);
-    const int buf = c & 1;
+  float gacc = 0.0f;
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int st = 0; st < kRK / 16; ++st) {
       const int ko = st * 16 + half * 8;
@@ -104,8 +127,53 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bm, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
     }
-    if (more) store(buf ^ 1);
-    __syncthreads();
+    if (gate) {
+      const uint4* xs = reinterpret_cast<const uint4*>(&As[buf][grow * kRRow + gq * 16]);
+      const float4* gs = reinterpret_cast<const float4*>(&Gs[buf][gq * 16]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 xv = xs[i];
+        const float4 g0 = gs[2 * i], g1 = gs[2 * i + 1];
+        gacc = __builtin_fmaf(bf16_to_f32(xv.x & 0xFFFFu), g0.x, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.x >> 16), g0.y, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.y & 0xFFFFu), g0.z, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.y >> 16), g0.w, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.z & 0xFFFFu), g1.x, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.z >> 16), g1.y, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.w & 0xFFFFu), g1.z, gacc);
+        gacc = __builtin_fmaf(bf16_to_f32(xv.w >> 16), g1.w, gacc);
+      }
+    }
+  };
+
+  // LDS buffer c & 1 holds chunk c; the registers of chunk c + 1 are in flight meanwhile
+  bf16x8_t xa0[2], xa1[2];
+  float4 wb0[4], wb1[4];
+  float g0, g1;
+  load(xa0, wb0, g0, 0);
+  load(xa1, wb1, g1, 1);
+  store(xa0, wb0, g0, 0);
+  barrier();
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    load(xa0, wb0, g0, c + 2);
+    compute(0);
+    store(xa1, wb1, g1, 1);
+    barrier();
+    load(xa1, wb1, g1, c + 3);
+    compute(1);
+    store(xa0, wb0, g0, 0);
+    barrier();
+  }
+  if (c < nchunks) compute(0);  // odd chunk count: the last chunk is in buffer 0
+  // drain the clamped tail loads before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (gate) {
+    gacc += __shfl_xor(gacc, 1, 64);
+    gacc += __shfl_xor(gacc, 2, 64);
+    const int t = t0 + grow;
+    if (gq == 0 && t < T) sgate[t] = 1.0f / (1.0f + __expf(-gacc));
   }
   // D layout of the 32x32 tile: register i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
   // column l%32.
@@ -119,10 +187,13 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
   }
 }
 
-hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias, int T,
-                                     int E, int H, float* logits, hipStream_t s) {
-  dim3 grid((E + 63) / 64, (T + 63) / 64);
-  hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, s, x, w, bias, T, E, H, logits);
+hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias,
+                                     const float* wg, int T, int E, int H, float* logits,
+                                     float* sgate, hipStream_t s) {
+  const int n_etiles = (E + 63) / 64, ntiles = n_etiles * ((T + 63) / 64);
+  const int grid = (ntiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(k_router_mfma, dim3(grid), dim3(256), 0, s, x, w, bias, wg, T, E, H,
+                     n_etiles, ntiles, logits, sgate);
   return hipGetLastError();
 }
 
