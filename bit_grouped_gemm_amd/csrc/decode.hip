@@ -413,10 +413,18 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
       const int tk = t0 + b * NW;
       if (tk < nB) {  // uniform over the wave
         const int d = tk / F, f = tk % F;
-        const int m = R.ent_m[d], row0 = R.ent_row0[d];
-        float v[2 * TC];
-        pair_dots<TC>(w[b], xs, H, lane, R.row_tok + row0, m, v);
-        pair_finish<TC>(v, lane, m, f, p.b.a, [&](int j) { return (size_t)(row0 + j) * F; });
+        const int m = __builtin_amdgcn_readfirstlane(R.ent_m[d]);
+        const int row0 = R.ent_row0[d];
+        auto a_row = [&](int j) { return (size_t)(row0 + j) * F; };
+        if (TC > 1 && m == 1) {  // most experts of a small batch serve one token
+          float v[2];
+          pair_dots<1>(w[b], xs, H, lane, R.row_tok + row0, 1, v);
+          pair_finish<1>(v, lane, 1, f, p.b.a, a_row);
+        } else {
+          float v[2 * TC];
+          pair_dots<TC>(w[b], xs, H, lane, R.row_tok + row0, m, v);
+          pair_finish<TC>(v, lane, m, f, p.b.a, a_row);
+        }
       }
     }
   };
@@ -506,7 +514,7 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
       const int d = wave + 4 * (i0 + b);
       const bool sh = d == D;
       const int Kd = sh ? Fs : F;
-      const int m = sh ? T : R.ent_m[d];
+      const int m = __builtin_amdgcn_readfirstlane(sh ? T : R.ent_m[d]);
       const int row0 = sh ? 0 : R.ent_row0[d];
       const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
       uint32_t wd[16];
@@ -515,6 +523,24 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
       dequant8(dw[b].q.y, ds, db, wd + 4);
       dequant8(dw[b].q.z, ds, db, wd + 8);
       dequant8(dw[b].q.w, ds, db, wd + 12);
+      if (TC > 1 && m == 1) {
+        // one token (bit t of the mask): every lane of the group ends with the row's sum
+        float one[1] = {0.0f};
+        if (sl < (Kd >> 5)) {
+          const uint4* av = reinterpret_cast<const uint4*>(abase + (size_t)row0 * F + 32 * sl);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 a4 = av[q];
+            one[0] = dot2_bf16(a4.x, wd[4 * q + 0], one[0]);
+            one[0] = dot2_bf16(a4.y, wd[4 * q + 1], one[0]);
+            one[0] = dot2_bf16(a4.z, wd[4 * q + 2], one[0]);
+            one[0] = dot2_bf16(a4.w, wd[4 * q + 3], one[0]);
+          }
+        }
+        group_reduce<1, 16>(one, sl);
+        if (sl < T && ((tmask >> sl) & 1u)) acc = __builtin_fmaf(R.row_w[row0], one[0], acc);
+        continue;
+      }
       float dots[TC];
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
@@ -637,7 +663,7 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const size_t lds_x = (size_t)d.T * d.H * 2;
   const size_t lds_b = lds_x + decode_b_lds_words(d) * 4;
   const size_t a_bytes = ((size_t)d.TK() * d.F + (size_t)d.T * d.Fs) * 2;
-  const int HG = d.T <= 2 ? 1 : 2;  // output rows per 16-lane group
+  constexpr int HG = 1;  // output rows per 16-lane group
   const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4 + (size_t)4 * HG * 64 * 4;
   const bool a_lds = a_bytes + lds_c_route <= kDecLdsMax;
   const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
@@ -650,7 +676,7 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
     if (phase < 0 || phase == 1)                                                 \
       hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);             \
     if (phase < 0 || phase == 2) {                                               \
-      constexpr int HGV = TCV <= 2 ? 1 : 2;                                      \
+      constexpr int HGV = HG;                                                    \
       if (a_lds)                                                                 \
         hipLaunchKernelGGL((k_dec_c<TCV, HGV, true>), gC, blk, lds_c, s, p);     \
       else                                                                       \
