@@ -28,8 +28,9 @@ Readings where the pages are silent (each also listed with its reason in the des
 Rounding profiles:
   * "exact": no intermediate rounding at all (the mathematical definition).
   * "bf16": rounds (nearest, ties to even) exactly where [P1 "The Model ..."] says the
-    method's tensor operations take bf16: the reconstructed weights and the SwiGLU output
-    that feeds the down projection. Everything else stays fp64.
+    method's tensor operations take bf16: the reconstructed weights, the SwiGLU output that
+    feeds the down projection, and each expert's output (routed and shared), which feeds the
+    weighted combine. Everything else stays fp64.
 
 Every function here is pinned by tests/test_oracle*.py against closed forms, brute force
 or invariants; no function is "parity unpinned".
@@ -152,11 +153,13 @@ def expert_ffn(x, wg, wu, wd, profile: str = "exact") -> np.ndarray:
     """FFN(x) = Wd . (silu(Wg . x) * (Wu . x)) for rows x [n, H] (fp64 values).
 
     In the "bf16" profile the SwiGLU output, which feeds the down projection's tensor
-    operation, is rounded to bf16."""
+    operation, and the expert's output, which feeds the weighted combine, are rounded to
+    bf16."""
     a = silu(x @ wg.T) * (x @ wu.T)
     if profile == "bf16":
         a = round_to_bf16(a)
-    return a @ wd.T
+    y = a @ wd.T
+    return round_to_bf16(y) if profile == "bf16" else y
 
 
 def _mat(proj, e, profile):

@@ -271,6 +271,46 @@ def test_expert_ffn_constant_weight_closed_form():
         assert np.allclose(y[t], F * cd * a, rtol=1e-14, atol=0)
 
 
+def _rne_bf16_via_f32_bits(v: float) -> float:
+    """Nearest bf16 of a value that fp32 holds exactly, by integer rounding of its fp32 bits
+    (ties to even): an implementation independent of the oracle's frexp-based rounding."""
+    b = int(np.array([v], np.float32).view(np.uint32)[0])
+    assert float(np.array([b], np.uint32).view(np.float32)[0]) == v
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return float(np.array([r], np.uint32).view(np.float32)[0])
+
+
+def test_expert_ffn_bf16_profile_closed_form():
+    """bf16 profile: the SwiGLU output and the expert output are each rounded to bf16
+    ([P1 "The Model ..."]: the tensor operations, down projection and weighted combine, take
+    bf16 inputs). Constant weights give y = F*cd*bf16(a) before the last rounding; F*cd = 1.5
+    makes that value need 9 significant bits, so the output rounding is exercised."""
+    H, F = 128, 64
+    cg, cu, cd = 0.015625, 0.0078125, 0.0234375          # bf16-exact constants, F*cd = 1.5
+    x = np.array([[1.0] * 64 + [-0.5] * 64, [2.0] * 128, [0.75] * 128])
+    wg = O.dequant(*[a[0] for a in _const_proj(F, H, cg)], "bf16")
+    wu = O.dequant(*[a[0] for a in _const_proj(F, H, cu)], "bf16")
+    wd = O.dequant(*[a[0] for a in _const_proj(H, F, cd)], "bf16")
+    y = O.expert_ffn(x, wg, wu, wd, "bf16")
+    y_exact = O.expert_ffn(x, wg, wu, wd)
+    rounded_somewhere = False
+    for t in range(x.shape[0]):
+        sx = float(x[t].sum())
+        g, u = cg * sx, cu * sx
+        a64 = g / (1 + math.exp(-g)) * u
+        a_b = _rne_bf16_via_f32_bits(float(np.float32(a64)))
+        # going through fp32 first decides the same bf16 as rounding a64 directly unless a64
+        # lies within one fp32 step of a bf16 midpoint
+        ulp_bf16 = 2.0 ** (math.frexp(a_b)[1] - 8)
+        mid = a_b + math.copysign(ulp_bf16 / 2, a64 - a_b)
+        assert abs(a64 - mid) > 2.0 ** (math.frexp(a64)[1] - 23)
+        want = _rne_bf16_via_f32_bits(F * cd * a_b)          # F*cd*a_b is exact in fp32
+        assert np.all(y[t] == want), (t, y[t][:2], want)
+        rounded_somewhere |= want != F * cd * a_b
+        assert np.allclose(y[t], y_exact[t], rtol=2.0 ** -7, atol=0)
+    assert rounded_somewhere
+
+
 def _tiny_layer_with(routed_zero=False, identical=False, seed=0):
     shape = synth.SHAPES["tiny"]
     L = synth.make_layer(shape, seed=seed)
