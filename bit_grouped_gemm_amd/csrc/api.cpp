@@ -91,7 +91,7 @@ Layout layout_of(const Dims& d, int flags) {
   L.a = o;       o = align_up(o + (TK * d.F + (size_t)d.T * d.Fs) * 2);
   L.end_no_y = o;
   L.y = o;
-  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) o = align_up(o + (TK + d.T) * d.H * 4);
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) o = align_up(o + (TK + d.T) * d.H * 2);  // bf16
   L.total = o;
   return L;
 }
@@ -222,7 +222,7 @@ int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* 
         return launch_gemm_w4(kDownAtomic, pd, mb, s);
       });
     } else {
-      float* y = at<float>(ws, L.y);
+      uint16_t* y = at<uint16_t>(ws, L.y);
       step([&] {
         const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN, a, &plan, nullptr, nullptr, y);
         return launch_gemm_w4(kDownStore, pd, mb, s);
@@ -337,7 +337,7 @@ int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void*
   const Layout L = layout_of(d, 0);
   if (!workspace) return MOE_INVALID_ARG;
   if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
-  float* y = at<float>(workspace, L.y);
+  uint16_t* y = at<uint16_t>(workspace, L.y);
   const GemmParams p = gemm_params(desc, d, MOE_GEMM_DOWN, in, plan, nullptr, nullptr, y);
   if (launch_gemm_w4(kDownStore, p, mb, s) != hipSuccess) return MOE_HIP_ERROR;
   return hip_status(launch_combine(y, plan->slot_pos, topk_w,
@@ -345,9 +345,9 @@ int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void*
                                    static_cast<float*>(out), s));
 }
 
-int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
-                const float* topk_w, const float* shared_y, const float* shared_gate, int32_t T,
-                float* out, void* stream) {
+int moe_combine(const moe_layer_desc_t* desc, const uint16_t* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const uint16_t* shared_y, const float* shared_gate,
+                int32_t T, float* out, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_INVALID_ARG;

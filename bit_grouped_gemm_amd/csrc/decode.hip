@@ -21,10 +21,11 @@
 //     experts' gate/up rows (a 1 KiB row per wave, 16 bytes per lane), dequantise them in
 //     registers and store A = bf16(silu(G) * U); workgroup 0 also stores the per-expert route
 //     record for C;
-//   C (k_dec_c): down projection fused with the weighted combine. The route record and the
-//     activations are staged in LDS; each 16-lane group owns output rows, the four waves of a
-//     workgroup walk interleaved quarters of the entry list (the shared expert last), and their
-//     partial sums are added in LDS in a fixed order, so the result is deterministic.
+//   C (k_dec_c): down projection fused with the weighted combine of the bf16-rounded expert
+//     outputs. The route record and the activations are staged in LDS; each 16-lane group
+//     owns output rows, the four waves of a workgroup walk interleaved quarters of the entry
+//     list (the shared expert last), and their partial sums are added in LDS in a fixed
+//     order, so the result is deterministic.
 // Every selected weight byte is read from HBM once per call.
 #include "moe_internal.h"
 
@@ -538,7 +539,8 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
           }
         }
         group_reduce<1, 16>(one, sl);
-        if (sl < T && ((tmask >> sl) & 1u)) acc = __builtin_fmaf(R.row_w[row0], one[0], acc);
+        if (sl < T && ((tmask >> sl) & 1u))
+          acc = __builtin_fmaf(R.row_w[row0], round_bf16(one[0]), acc);
         continue;
       }
       float dots[TC];
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
         wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
       }
       const float val = TC == 1 ? dots[0] : __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
-      if (mine) acc = __builtin_fmaf(wgt, val, acc);
+      if (mine) acc = __builtin_fmaf(wgt, round_bf16(val), acc);  // the expert output in bf16
     }
   };
 

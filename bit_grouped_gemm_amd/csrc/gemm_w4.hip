@@ -316,7 +316,8 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
   // 16-byte segments permuted by (r >> 2), so that rows r and r + 4, written by the two halves
   // of the wave, fall in different banks) and written back in 16-byte pieces.
   char* tile = lds.pick(wave);
-  if (MODE == kGateUp) {
+  static_assert(MODE == kGateUp, "the down projection has its own kernel");
+  {
     constexpr int kPairs = NC / 2;
     constexpr int kRB = kPairs * 64;      // bytes per staged row (bf16)
     constexpr int kSegs = kRB / 16;
@@ -346,62 +347,6 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
       const int seg = q ^ ((r >> 2) & (kSegs - 1));
       const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kRB + seg * 16);
       if (r < m_len && qval) *reinterpret_cast<uint4*>(orow + (size_t)r * ncols) = v;
-    }
-  } else if (MODE == kDownStore) {
-    constexpr int kRB = NC * 128;         // bytes per staged row (fp32)
-    constexpr int kSegs = kRB / 16;
-    constexpr int kTPP = kArrBytes / (32 * kRB);  // row tiles per staging pass
-    constexpr int kRowsPerPass = 64 / kSegs;
-    const int q = lane % kSegs;
-    const bool qval = wcol0 + 4 * q < ncols;
-#pragma unroll
-    for (int h0 = 0; h0 < NT; h0 += kTPP) {
-#pragma unroll
-      for (int mt = h0; mt < NT && mt < h0 + kTPP; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (mt - h0) * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-          for (int t = 0; t < NC; ++t) {
-            const int c = 32 * t + n;
-            const int seg = (c >> 2) ^ ((r >> 2) & (kSegs - 1));
-            *reinterpret_cast<float*>(tile + r * kRB + seg * 16 + 4 * (c & 3)) = acc[mt][t][i];
-          }
-        }
-      float* orow = static_cast<float*>(p.out) + (size_t)(row0 + 32 * h0) * p.out_ld + wcol0 + 4 * q;
-      const int nrows = (NT - h0 < kTPP ? NT - h0 : kTPP) * 32;
-#pragma unroll
-      for (int pass = 0; pass < kTPP * 32 / kRowsPerPass; ++pass) {
-        const int r = pass * kRowsPerPass + lane / kSegs;
-        const int seg = q ^ ((r >> 2) & (kSegs - 1));
-        if (r < nrows) {
-          const float4 v = *reinterpret_cast<const float4*>(tile + r * kRB + seg * 16);
-          if (32 * h0 + r < m_len && qval) *reinterpret_cast<float4*>(orow + (size_t)r * p.out_ld) = v;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (r >= m_len) continue;
-        int tok;
-        float wgt;
-        if (shared) {
-          tok = m0 + r;
-          wgt = p.shared_gate[tok];
-        } else {
-          const int slot = p.sorted_slots[row0 + r];
-          tok = slot / p.K;
-          wgt = p.topk_w[slot];
-        }
-        float* out = static_cast<float*>(p.out) + (size_t)tok * p.out_ld;
-#pragma unroll
-        for (int t = 0; t < NC; ++t)
-          if (tval[t]) atomicAdd(out + col[t], wgt * acc[mt][t][i]);
-      }
     }
   }
 }
@@ -624,18 +569,27 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
   if (!wave_active) return;
 
   // ---- epilogue. D layout (32x32): register i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-  // column l%32 of the tile; each store instruction writes two 128-byte row pieces.
+  // column l%32 of the tile. The expert outputs are rounded to bf16. Stores: an even lane n
+  // writes tile 0's columns (n, n + 1), an odd lane tile 1's columns (n - 1, n), each pair
+  // as one 32-bit word after a neighbour exchange, so a store instruction writes two 128-byte
+  // rows (64 columns each).
+  const bool odd = (n & 1) != 0;
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (r >= m_len) continue;
       if (MODE == kDownStore) {
-        float* out = static_cast<float*>(p.out) + (size_t)(row0 + r) * p.out_ld;
-        out[col0] = acc[mt][0][i];
-        if (tile1) out[col1] = acc[mt][1][i];
-      } else {
+        const float v0 = acc[mt][0][i], v1 = acc[mt][1][i];
+        const float other = __shfl_xor(odd ? v0 : v1, 1, 64);  // the pair's other half
+        const uint32_t w = odd ? pack_bf16x2(other, v1) : pack_bf16x2(v0, other);
+        uint16_t* out = static_cast<uint16_t*>(p.out) + (size_t)(row0 + r) * p.out_ld;
+        if (r < m_len && (!odd || tile1))
+          *reinterpret_cast<uint32_t*>(out + (odd ? col1 - 1 : col0)) = w;
+        continue;
+      }
+      if (r >= m_len) continue;
+      {
         int tok;
         float wgt;
         if (shared) {
@@ -647,8 +601,8 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
           wgt = p.topk_w[slot];
         }
         float* out = static_cast<float*>(p.out) + (size_t)tok * p.out_ld;
-        atomicAdd(out + col0, wgt * acc[mt][0][i]);
-        if (tile1) atomicAdd(out + col1, wgt * acc[mt][1][i]);
+        atomicAdd(out + col0, wgt * round_bf16(acc[mt][0][i]));
+        if (tile1) atomicAdd(out + col1, wgt * round_bf16(acc[mt][1][i]));
       }
     }
   }

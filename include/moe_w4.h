@@ -19,7 +19,9 @@
  *   y[t] = sum_{e in topk(t)} p[t,e] * Wd_e(silu(Wg_e x[t]) * (Wu_e x[t]))
  *        + sigmoid(wg . x[t]) * Wd_s(silu(Wg_s x[t]) * (Wu_s x[t]))
  * with p = softmax over the selected router logits, ties in the top-k going to the lower
- * expert index, and every W = scale * q + bias dequantised per group of 64 inputs.
+ * expert index, and every W = scale * q + bias dequantised per group of 64 inputs. The
+ * inputs of the tensor operations are bf16 [P1 "The Model ..."]: the dequantised weights,
+ * the SwiGLU output, and each expert's output as the weighted combine takes it.
  *
  * Conventions for every entry point:
  *   - bf16 values are passed as uint16_t bit patterns.
@@ -114,7 +116,7 @@ typedef struct {
 /* moe_grouped_gemm_w4 `which` */
 enum {
   MOE_GEMM_GATE_UP = 0,             /* out = A [T*K*F + T*Fs] bf16: silu(G)*U per grouped row */
-  MOE_GEMM_DOWN = 1,                /* out = Y [(T*K + T), H] fp32, unweighted, grouped rows  */
+  MOE_GEMM_DOWN = 1,                /* out = Y [(T*K + T), H] bf16, unweighted, grouped rows  */
   MOE_GEMM_DOWN_COMBINE = 2,        /* out = y [T, H] fp32, the combined layer output         */
   MOE_GEMM_DOWN_COMBINE_ATOMIC = 3  /* as 2, combined with fp32 atomics (order not fixed)     */
 };
@@ -161,10 +163,12 @@ int moe_permute(const moe_layer_desc_t* desc, const int32_t* topk_idx, int32_t T
  *   GATE_UP: in = x [T, H] bf16 (rows gathered through plan->sorted_slots; the shared
  *            expert reads x in token order); out = A bf16, routed rows [T*K, F] in grouped
  *            order followed by shared rows [T, Fs]: A = bf16(silu(x Wg^T) * (x Wu^T)).
- *   DOWN:    in = A as above; out = Y [T*K + T, H] fp32 = A Wd^T per grouped row.
+ *   DOWN:    in = A as above; out = Y [T*K + T, H] bf16 = bf16(A Wd^T) per grouped row
+ *            (fp32 accumulation, rounded to nearest even once).
  *   DOWN_COMBINE(_ATOMIC): in = A; out = y [T, H] fp32 =
  *            sum_k topk_w[t,k] Y[slot_pos[t*K+k]] + shared_gate[t] * Y[T*K + t]
- *            (overwritten, not accumulated). Needs topk_w and, when Fs > 0, shared_gate.
+ *            with Y the bf16-rounded rows as in DOWN, summed in fp32 (overwritten, not
+ *            accumulated). Needs topk_w and, when Fs > 0, shared_gate.
  * For T <= 16 (and F, Fs <= 512, T*H <= 32768) GATE_UP and DOWN_COMBINE run the decode
  * path's GEMV kernels (the same ones moe_layer_forward uses for such T; DOWN_COMBINE is then
  * deterministic and needs no workspace).
@@ -173,12 +177,13 @@ int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void*
                         const moe_plan_t* plan, const float* topk_w, const float* shared_gate,
                         void* out, void* workspace, size_t ws_bytes, void* stream);
 
-/* Weighted combine: y[t] = sum_k topk_w[t,k] * y_perm[slot_pos[t*K+k]]
+/* Weighted combine [P1 "The Model ..."]: y[t] = sum_k topk_w[t,k] * y_perm[slot_pos[t*K+k]]
  *                        + shared_gate[t] * shared_y[t]     (the shared term only if Fs > 0)
- * y_perm [T*K, H] fp32 (grouped rows), shared_y [T, H] fp32, out [T, H] fp32 (overwritten).
+ * y_perm [T*K, H] bf16 (grouped rows, as moe_grouped_gemm_w4 DOWN writes them), shared_y
+ * [T, H] bf16, out [T, H] fp32 (overwritten), products and sums in fp32.
  * Deterministic: terms are added in rank order k = 0..K-1, then the shared term. */
-int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
-                const float* topk_w, const float* shared_y, const float* shared_gate,
+int moe_combine(const moe_layer_desc_t* desc, const uint16_t* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const uint16_t* shared_y, const float* shared_gate,
                 int32_t T, float* out, void* stream);
 
 /* The whole layer: x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path, larger T

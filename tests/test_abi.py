@@ -66,8 +66,8 @@ def test_workspace_sizes():
     d = fake_desc()
     base = ws_bytes(d, 4096)
     atomic = ws_bytes(d, 4096, M.MOE_FLAG_ATOMIC_COMBINE)
-    # the unfused combine stages fp32 rows for T*K + T grouped rows
-    assert base - atomic >= (4096 * 8 + 4096) * 2048 * 4
+    # the unfused combine stages bf16 rows for T*K + T grouped rows
+    assert base - atomic >= (4096 * 8 + 4096) * 2048 * 2  # the bf16 expert outputs
     assert ws_bytes(d, 1) < ws_bytes(d, 8) < base
     assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 4096) == 32768 // M.MOE_BLOCK_M + 256 + 4096 // M.MOE_BLOCK_M
     assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 1) == 1 + 8 + 1
