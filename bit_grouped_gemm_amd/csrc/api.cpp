@@ -74,7 +74,8 @@ Layout layout_of(const Dims& d, int flags) {
   size_t o = 0;
   const size_t TK = (size_t)d.T * d.K;
   const int nchunks = (int)((TK + kChunkSlots - 1) / kChunkSlots);
-  L.logits = o;  o = align_up(o + (size_t)d.T * (d.E + 1) * 4);
+  // up to kRouterMaxSplits partial slices of [T, E+1] (prefill router, split-K)
+  L.logits = o;  o = align_up(o + (size_t)kRouterMaxSplits * d.T * (d.E + 1) * 4);
   L.end_route = o;
   L.hist = o;    o = align_up(o + (size_t)nchunks * (d.E + 1) * 4);
   L.end_permute = o;
@@ -115,13 +116,16 @@ int run_route(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, in
   hipError_t e;
   if (decode) {
     e = launch_router_logits_gemv(x, desc->router_w, desc->router_bias, d.T, d.E, d.H, logits, s);
-  } else {  // the MFMA router forms the shared gate itself
-    e = launch_router_logits_mfma(x, desc->router_w, desc->router_bias, wg, d.T, d.E, d.H, logits,
-                                  sgate, s);
-    wg = nullptr;
+    if (e != hipSuccess) return MOE_HIP_ERROR;
+    return hip_status(launch_topk(logits, 1, d.E, false, x, wg, d.T, d.E, d.K, d.H, idx, w,
+                                  sgate, s));
   }
+  // the MFMA router leaves partial slices, with the shared-gate logit in column E
+  e = launch_router_logits_mfma(x, desc->router_w, desc->router_bias, wg, d.T, d.E, d.H, logits,
+                                s);
   if (e != hipSuccess) return MOE_HIP_ERROR;
-  return hip_status(launch_topk(logits, x, wg, d.T, d.E, d.K, d.H, idx, w, sgate, s));
+  return hip_status(launch_topk(logits, router_splits(d.T, d.E, d.H), d.E + 1, wg != nullptr, x,
+                                nullptr, d.T, d.E, d.K, d.H, idx, w, sgate, s));
 }
 
 GemmParams gemm_params(const moe_layer_desc_t* desc, const Dims& d, int which, const void* in,
@@ -207,8 +211,11 @@ int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* 
     step([&] { return launch_dec_down(d, *desc, a, plan, w, sgate, out, s); });
   } else {
     step([&] { return launch_router_logits_mfma(x, desc->router_w, desc->router_bias, wg, d.T,
-                                                d.E, d.H, logits, sgate, s); });
-    step([&] { return launch_topk(logits, x, nullptr, d.T, d.E, d.K, d.H, idx, w, sgate, s); });
+                                                d.E, d.H, logits, s); });
+    step([&] {
+      return launch_topk(logits, router_splits(d.T, d.E, d.H), d.E + 1, wg != nullptr, x, nullptr,
+                         d.T, d.E, d.K, d.H, idx, w, sgate, s);
+    });
     step([&] { return launch_permute(idx, d, d.Fs > 0, at<int32_t>(ws, L.hist), plan, s); });
     step([&] {
       const GemmParams pg = gemm_params(desc, d, MOE_GEMM_GATE_UP, x, &plan, nullptr, nullptr, a);

@@ -41,14 +41,20 @@ struct GemmParams {
 enum GemmMode { kGateUp = 0, kDownStore = 1, kDownAtomic = 2 };
 
 // Launchers (return the launch status).
-// wg != nullptr: also writes sgate[t] = sigmoid(x_t . wg).
+// Prefill router logits as router_splits(T, E, H) partial slices [S][T][E+1] (split-K over the
+// inputs); column E of a slice holds the partial shared-gate logit x . wg when wg != nullptr.
+constexpr int kRouterMaxSplits = 8;
+int router_splits(int T, int E, int H);
 hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias,
                                      const float* wg, int T, int E, int H, float* logits,
-                                     float* sgate, hipStream_t s);
+                                     hipStream_t s);
 hipError_t launch_router_logits_gemv(const uint16_t* x, const float* w, const float* bias, int T,
                                      int E, int H, float* logits, hipStream_t s);
-hipError_t launch_topk(const float* logits, const uint16_t* x, const float* wg, int T, int E,
-                       int K, int H, int32_t* idx, float* w, float* sgate, hipStream_t s);
+// Top-k over the sum of S logit slices [S][T][ld]; the shared gate from column E of the slices
+// (gate_col) or from x . wg (wg != nullptr), else not written.
+hipError_t launch_topk(const float* logits, int S, int ld, bool gate_col, const uint16_t* x,
+                       const float* wg, int T, int E, int K, int H, int32_t* idx, float* w,
+                       float* sgate, hipStream_t s);
 hipError_t launch_count(const int32_t* idx, int TK, int E, int32_t* counts, hipStream_t s);
 hipError_t launch_route_small(const float* logits, const uint16_t* x, const float* wg,
                               const Dims& d, int32_t* idx, float* w, float* sgate,

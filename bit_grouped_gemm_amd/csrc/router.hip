@@ -24,10 +24,13 @@ namespace moe {
 //
 // The global loads run two chunks ahead of the MFMAs (two register sets), and the barrier
 // between chunks waits only for the LDS stores, so the prefetch stays in flight across it.
+// When there are few token tiles the inputs are split into S ranges (split-K), so that the
+// chip has enough workgroups: split s writes its partial logits to slice s of an [S, T, E+1]
+// array, and the top-k kernel adds the S slices in a fixed order.
 // Workgroups are dispatched round-robin over the 8 XCDs; XCD i takes a contiguous range of
-// tiles, so the expert tiles of one token tile read x through the same L2.
-// The workgroups of the first expert tile also form the shared-expert gate logit x . wg in fp32
-// from the x chunks they hold in LDS.
+// tiles, so the expert tiles of one token tile (and split) read x through the same L2.
+// The workgroups of the first expert tile also form the partial shared-expert gate logit
+// x . wg in fp32 from the x chunks they hold in LDS (column E of the slice).
 namespace {
 constexpr int kRK = 64;        // inputs per K-chunk
 constexpr int kRRow = kRK + 8; // padded LDS row (bf16 elements)
@@ -48,9 +51,9 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
                                                         const float* __restrict__ w,
                                                         const float* __restrict__ bias,
                                                         const float* __restrict__ wg, int T,
-                                                        int E, int H, int n_etiles, int ntiles,
-                                                        float* __restrict__ logits,
-                                                        float* __restrict__ sgate) {
+                                                        int E, int H, int n_etiles,
+                                                        int n_ttiles, int ntiles, int cps,
+                                                        float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * kRRow];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][64 * kRRow];
   __shared__ __attribute__((aligned(16))) float Gs[2][kRK];
@@ -59,15 +62,17 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
   if (tile >= ntiles) return;  // whole workgroup, before any barrier
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = (tile / n_etiles) * 64, e0 = (tile % n_etiles) * 64;
+  const int split = tile / (n_ttiles * n_etiles), rem = tile % (n_ttiles * n_etiles);
+  const int t0 = (rem / n_etiles) * 64, e0 = (rem % n_etiles) * 64;
   const bool gate = wg != nullptr && e0 == 0;
   const float* wgp = wg != nullptr ? wg : w;  // loads stay unconditional; unused without a gate
-  const int nchunks = H / kRK;
+  const int c0 = split * cps;                      // this split's first K-chunk
+  const int nchunks = min(cps, H / kRK - c0);      // and its chunk count (>= 1)
 
   // one chunk's registers: x (64 rows x 8 segments of 8 bf16, two per thread), router rows
   // (64 rows x 16 float4, four per thread) and the shared gate weight k0 + (tid & 63)
   auto load = [&](bf16x8_t (&ra)[2], float4 (&rb)[4], float& rg, int c) {
-    const int k0 = min(c, nchunks - 1) * kRK;
+    const int k0 = (c0 + min(c, nchunks - 1)) * kRK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + 256 * i, row = v >> 3, seg = v & 7;
@@ -169,31 +174,43 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
   // drain the clamped tail loads before the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
+  const int ld = E + 1;
+  float* slice = logits + (size_t)split * T * ld;
   if (gate) {
     gacc += __shfl_xor(gacc, 1, 64);
     gacc += __shfl_xor(gacc, 2, 64);
     const int t = t0 + grow;
-    if (gq == 0 && t < T) sgate[t] = 1.0f / (1.0f + __expf(-gacc));
+    if (gq == 0 && t < T) slice[(size_t)t * ld + E] = gacc;
   }
   // D layout of the 32x32 tile: register i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-  // column l%32.
+  // column l%32. The bias goes into split 0 only.
   const int e = e0 + (wave & 1) * 32 + r;
   if (e >= E) return;
-  const float bv = bias ? bias[e] : 0.0f;
+  const float bv = (bias != nullptr && split == 0) ? bias[e] : 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = t0 + (wave >> 1) * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (t < T) logits[(size_t)t * E + e] = acc[i] + bv;
+    if (t < T) slice[(size_t)t * ld + e] = acc[i] + bv;
   }
+}
+
+int router_splits(int T, int E, int H) {
+  const int base = ((E + 63) / 64) * ((T + 63) / 64);
+  const int nchunks = H / kRK;
+  int S = 1;
+  while (S < kRouterMaxSplits && base * S * 2 <= 512 && nchunks % (2 * S) == 0) S *= 2;
+  return S;
 }
 
 hipError_t launch_router_logits_mfma(const uint16_t* x, const float* w, const float* bias,
                                      const float* wg, int T, int E, int H, float* logits,
-                                     float* sgate, hipStream_t s) {
-  const int n_etiles = (E + 63) / 64, ntiles = n_etiles * ((T + 63) / 64);
+                                     hipStream_t s) {
+  const int S = router_splits(T, E, H);
+  const int n_etiles = (E + 63) / 64, n_ttiles = (T + 63) / 64;
+  const int ntiles = n_etiles * n_ttiles * S;
   const int grid = (ntiles + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL(k_router_mfma, dim3(grid), dim3(256), 0, s, x, w, bias, wg, T, E, H,
-                     n_etiles, ntiles, logits, sgate);
+                     n_etiles, n_ttiles, ntiles, (H / kRK) / S, logits);
   return hipGetLastError();
 }
 
@@ -262,13 +279,15 @@ hipError_t launch_router_logits_gemv(const uint16_t* x, const float* w, const fl
 }
 
 // ------------------------------------------------------------------ top-k + gates
-// One wave per token. Lane l holds logits e = l + 64*j. K rounds of a wave arg-max ordered
-// by (larger logit, then lower expert index) give the top-k in rank order; lane r keeps the
-// rank-r winner. Weights: softmax over the selected logits, which equals a softmax over all
-// experts renormalised over the selected ones. The shared expert's gate is sigmoid(x . wg).
+// One wave per token. Lane l holds logits e = NJ*l + j (the sum of the S split slices, added in
+// slice order). K rounds of a wave arg-max ordered by (larger logit, then lower expert index)
+// give the top-k in rank order; lane r keeps the rank-r winner. Weights: softmax over the
+// selected logits, which equals a softmax over all experts renormalised over the selected
+// ones. The shared expert's gate is sigmoid(x . wg): from column E of the slices when
+// gate_col, otherwise formed here from x and wg (when wg is given).
 template <int NJ>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
-                                              const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int S, int ld,
+                                              int gate_col, const uint16_t* __restrict__ x,
                                               const float* __restrict__ wg, int T, int E, int K,
                                               int H, int32_t* __restrict__ idx,
                                               float* __restrict__ wout,
@@ -276,24 +295,43 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // no barriers in this kernel
+  const size_t slice = (size_t)T * ld;
+  const float* lt = logits + (size_t)t * ld;
+  float v[NJ];
+  load_logits<NJ>(lt, E, lane, v);
+  for (int s = 1; s < S; ++s) {
+    float u[NJ];
+    load_logits<NJ>(lt + s * slice, E, lane, u);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v[j] += u[j];
+  }
   float my_v, my_w;
   int my_i;
-  wave_topk<NJ>(logits + (size_t)t * E, E, K, lane, my_v, my_i, my_w);
+  wave_topk_softmax<NJ>(v, E, K, lane, my_v, my_i, my_w);
   if (lane < K) {
     idx[(size_t)t * K + lane] = my_i;
     wout[(size_t)t * K + lane] = my_w;
   }
-  if (wg != nullptr) {
+  if (gate_col) {
+    if (lane == 0) {
+      float g = lt[E];
+      for (int s = 1; s < S; ++s) g += lt[s * slice + E];
+      sgate[t] = 1.0f / (1.0f + __expf(-g));
+    }
+  } else if (wg != nullptr) {
     const float g = shared_gate_logit(x + (size_t)t * H, wg, H, lane);
     if (lane == 0) sgate[t] = 1.0f / (1.0f + __expf(-g));
   }
 }
 
-hipError_t launch_topk(const float* logits, const uint16_t* x, const float* wg, int T, int E,
-                       int K, int H, int32_t* idx, float* w, float* sgate, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int S, int ld, bool gate_col, const uint16_t* x,
+                       const float* wg, int T, int E, int K, int H, int32_t* idx, float* w,
+                       float* sgate, hipStream_t s) {
   const dim3 grid((T + 3) / 4);
-#define MOE_TOPK(NJ) \
-  hipLaunchKernelGGL(k_topk<NJ>, grid, dim3(256), 0, s, logits, x, wg, T, E, K, H, idx, w, sgate)
+  const int gc = gate_col ? 1 : 0;
+#define MOE_TOPK(NJ)                                                                            \
+  hipLaunchKernelGGL(k_topk<NJ>, grid, dim3(256), 0, s, logits, S, ld, gc, x, wg, T, E, K, H, \
+                     idx, w, sgate)
   if (E <= 64)
     MOE_TOPK(1);
   else if (E <= 256)
