@@ -15,8 +15,10 @@
 //    register file. The K loop and the epilogue are compiled for 1..8 active row tiles.
 //  * The K loop runs over chunks of 64 inputs (one quantisation group). Activation rows
 //    (gathered through the permutation for gate/up) are copied per chunk straight from global
-//    memory into LDS with global_load_lds_dwordx4 (no staging registers). Four LDS buffers
-//    keep three chunks in flight while one is multiplied. A chunk row is 128 B; its 16-byte
+//    memory into LDS with global_load_lds_dwordx4 (no staging registers). Two LDS buffers
+//    keep the next chunk in flight while one is multiplied: measured on the full-size layer,
+//    deeper rings (up to seven chunks in flight) made the loop slower, not faster, because the
+//    extra copies in flight delayed the chunk being waited for. A chunk row is 128 B; its 16-byte
 //    segment g is stored at g ^ ((row >> 1) & 7), so the A-fragment reads of the MFMAs
 //    (32 rows, one segment each) are free of bank conflicts.
 //  * Packed weights go straight from HBM to registers: lane l owns column (l & 31) of a
@@ -40,7 +42,7 @@ constexpr int kRowBytes = kKC * 2;               // one activation row of a chun
 constexpr int kMT = kBlockM / 32;                // row tiles per block
 constexpr int kArrRows = 128;                    // rows of a chunk per LDS array
 constexpr int kArrBytes = kArrRows * kRowBytes;  // 16 KiB
-constexpr int kNArr = 8;                         // LDS arrays (128 KiB)
+constexpr int kNArr = 4;                         // LDS arrays (64 KiB)
 static_assert(kMT == 8 && kBlockM == 2 * kArrRows, "a chunk of a full block spans two arrays");
 }  // namespace
 
@@ -48,8 +50,7 @@ static_assert(kMT == 8 && kBlockM == 2 * kArrRows, "a chunk of a full block span
 struct LdsArrays {
   char* a[kNArr];
   __device__ __forceinline__ char* pick(int i) const {  // i uniform, not a compile-time constant
-    return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : i == 3 ? a[3]
-         : i == 4 ? a[4] : i == 5 ? a[5] : i == 6 ? a[6] : a[7];
+    return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
   }
 };
 
@@ -163,12 +164,11 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
   }
   const bool wave_active = tval[0];
 
-  // ---- chunk slots: blocks of up to 4 row tiles use one 16 KiB array per chunk and keep
-  // kNB - 1 = 7 chunks in flight; larger blocks use two arrays per chunk (rows 0-127, 128-255)
-  // and keep 3 in flight. Separate arrays let the compiler see that reads of one slot never
-  // depend on copies into another.
-  static_assert(NT <= 4 || NARR == kNArr, "blocks over 4 row tiles need all arrays");
-  constexpr int kNB = NT <= 4 ? NARR : NARR / 2;
+  // ---- chunk slots: kNB = 2 (one chunk in flight). Blocks of up to 4 row tiles use one
+  // 16 KiB array per chunk, larger blocks two (rows 0-127, 128-255). Separate arrays let the
+  // compiler see that reads of one slot never depend on copies into another.
+  static_assert(NARR == kNArr, "two chunk slots of up to two arrays");
+  constexpr int kNB = 2;
   auto slot_lo = [&](int k) -> char* { return NT <= 4 ? lds.a[k] : lds.a[2 * k]; };
   auto slot_hi = [&](int k) -> char* { return NT <= 4 ? lds.a[k] : lds.a[2 * k + 1]; };
 
@@ -365,11 +365,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4_gate_up(GemmParams p, int ns
   __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds2[kArrBytes];
   __shared__ __attribute__((aligned(1024))) char lds3[kArrBytes];
-  __shared__ __attribute__((aligned(1024))) char lds4[kArrBytes];
-  __shared__ __attribute__((aligned(1024))) char lds5[kArrBytes];
-  __shared__ __attribute__((aligned(1024))) char lds6[kArrBytes];
-  __shared__ __attribute__((aligned(1024))) char lds7[kArrBytes];
-  const LdsArrays lds{{lds0, lds1, lds2, lds3, lds4, lds5, lds6, lds7}};
+  const LdsArrays lds{{lds0, lds1, lds2, lds3}};
 
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int jd = kXcds * (local / nslices) + xcd;  // dispatch position
