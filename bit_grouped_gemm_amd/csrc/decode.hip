@@ -34,6 +34,9 @@ namespace moe {
 namespace {
 constexpr int kCH = 4;  // 16-byte chunks (32 inputs) per lane of a gate/up row (H <= 2048)
 constexpr int kNB = 4;  // down rows requested per batch by one 16-lane group
+// k_dec_b runs one 16-wave workgroup per CU: a single wave per CU derives the top-k, so the
+// selection rounds of different workgroups do not share a SIMD's issue slots.
+constexpr int kDecBWaves = 16;
 }  // namespace
 
 struct DecodeArgs {
@@ -237,9 +240,32 @@ __device__ void build_route(const Route& R, const int* sel_idx, const float* sel
   __syncthreads();
 }
 
+// Copy n 16-byte pieces from global memory to LDS with the NT threads of the workgroup, NB
+// pieces per thread in flight: each batch issues all its loads (indices past the end re-read
+// the last piece) before the first LDS write, so a batch costs one memory round trip.
+template <int NB, int NT>
+__device__ __forceinline__ void stage_pieces(uint4* dst, const uint4* __restrict__ src, int n) {
+  for (int v0 = threadIdx.x; v0 < n; v0 += NB * NT) {
+    uint4 t[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int v = v0 + b * NT;
+      t[b] = src[v < n ? v : n - 1];
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int v = v0 + b * NT;
+      if (v < n) dst[v] = t[b];
+    }
+  }
+}
+
+// x of up to TC tokens with NT threads (H <= 2048: at most TC*256/NT pieces per thread)
+template <int TC, int NT>
 __device__ __forceinline__ void stage_x(uint16_t* xs, const uint16_t* __restrict__ x, int n8) {
-  for (int v = threadIdx.x; v < n8; v += 256)
-    reinterpret_cast<uint4*>(xs)[v] = reinterpret_cast<const uint4*>(x)[v];
+  constexpr int per = (TC * 256 + NT - 1) / NT;
+  stage_pieces<(per < 8 ? per : 8), NT>(reinterpret_cast<uint4*>(xs),
+                                        reinterpret_cast<const uint4*>(x), n8);
 }
 
 // ============================================================================ A
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
   } else if (shared_task) {
     load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
   }
-  stage_x(xs, p.x, (T * H) >> 3);
+  stage_x<TC, 256>(xs, p.x, (T * H) >> 3);
   __syncthreads();
 
   if (router) {
@@ -327,12 +353,12 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
 // Grid-stride tasks (entry d, row f): one wave per gate row + up row, with the next task's rows
 // requested before the current one is used.
 template <int TC, int NJ>
-__global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
+__global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint4 smem[];
   const int T = p.T, H = p.H, E = p.E, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int NW = gridDim.x * 4, gw = blockIdx.x * 4 + wave;
+  const int NW = gridDim.x * kDecBWaves, gw = blockIdx.x * kDecBWaves + wave;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                  // [T, H]
   int* sel_idx = reinterpret_cast<int*>(xs + (size_t)T * H);        // [TK]
   float* sel_w = reinterpret_cast<float*>(sel_idx + TK);            // [TK]
@@ -346,9 +372,9 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
   float lv[NJ];
   if (wave < T) load_logits<NJ>(p.b.logits + (size_t)wave * E, E, lane, lv);
   const float glog = p.b.logits[(size_t)T * E + (tid < T ? tid : T - 1)];
-  stage_x(xs, p.x, (T * H) >> 3);
+  stage_x<TC, 64 * kDecBWaves>(xs, p.x, (T * H) >> 3);
   if (T > 1)
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += 64 * kDecBWaves) {
       cnt[e] = 0;
       tmask[e] = 0u;
     }
@@ -373,7 +399,7 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
     }
     __syncthreads();
   } else {
-    for (int t = wave; t < T; t += 4) {
+    for (int t = wave; t < T; t += kDecBWaves) {
       if (t != wave) load_logits<NJ>(p.b.logits + (size_t)t * E, E, lane, lv);
       float my_v, my_w;
       int my_i;
@@ -390,22 +416,21 @@ __global__ __launch_bounds__(256) void k_dec_b(DecodeArgs p) {
   }
   if (blockIdx.x == 0) {  // the route record for the down projection
     const int n = (int)route_words(TK, T);
-    for (int i = tid; i < n; i += 256) p.b.route[i] = R.nd[i];
+    for (int i = tid; i < n; i += 64 * kDecBWaves) p.b.route[i] = R.nd[i];
   }
   const int D = *R.nd;
 
   // Tasks task = gw + NW*i, in batches of kPB; the next batch's rows are requested before the
-  // current batch is used. Indices past the last task are clamped to it (wasted loads of one
-  // row, never used), so no load is conditional.
+  // current batch is used. A batch requests no rows past the last task.
   const int nB = D * F;
   constexpr int kPB = 2;
   const int step = kPB * NW;
   auto issue = [&](PairW (&w)[kPB], int t0) {
 #pragma unroll
     for (int b = 0; b < kPB; ++b) {
-      int tk = t0 + b * NW;
-      tk = tk < nB ? tk : nB - 1;
-      load_pair(w[b], p.gate, p.up, (size_t)R.ent_e[tk / F] * F + tk % F, H, lane);
+      const int tk = t0 + b * NW;
+      if (b == 0 || tk < nB)  // uniform over the wave; t0 < nB at every call
+        load_pair(w[b], p.gate, p.up, (size_t)R.ent_e[tk / F] * F + tk % F, H, lane);
     }
   };
   auto run = [&](const PairW (&w)[kPB], int t0) {
@@ -471,19 +496,16 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
 
   const int nw = (int)route_words(TK, T);
   for (int i = tid; i < nw; i += 256) R.nd[i] = p.b.route[i];
-  if (A_LDS)
-    for (size_t v = tid; v < a_elems / 8; v += 256)
-      reinterpret_cast<uint4*>(as)[v] = reinterpret_cast<const uint4*>(p.b.a)[v];
   __syncthreads();
   const int D = *R.nd;
   const int nD = D + (Fs > 0 ? 1 : 0);  // the shared expert is the last entry
   const int ni = wave < nD ? (nD - wave + 3) >> 2 : 0;  // entries of this wave
   const uint16_t* abase = A_LDS ? as : p.b.a;
 
-  // Entries i0 .. i0+kNB-1 of this wave for row h. Entries past the wave's list are clamped to
-  // the last entry and lanes past a short row re-read its last chunk (both never used), so every
-  // load is unconditional; the weight pointers are selected as values, not as references into
-  // the argument block (which would be read with vector loads and waited for).
+  // Entries i0 .. i0+kNB-1 of this wave for row h; none past the wave's list is requested.
+  // Lanes past a short row re-read its last chunk (never used), so the loads of an entry are
+  // unconditional; the weight pointers are selected as values, not as references into the
+  // argument block (which would be read with vector loads and waited for).
   const uint32_t* const rq = p.down.q;
   const uint16_t* const rs = p.down.scale;
   const uint16_t* const rb = p.down.bias;
@@ -493,8 +515,8 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
   auto load_down = [&](int h, int i0, DownW (&dw)[kNB]) {
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      int d = wave + 4 * (i0 + b);
-      d = d < nD ? d : nD - 1;
+      const int d = wave + 4 * (i0 + b);
+      if (d >= nD) break;  // uniform over the wave: no request past the wave's last entry
       const bool sh = d == D;
       const int Kd = sh ? Fs : F;
       const int c = sl < (Kd >> 5) ? sl : (Kd >> 5) - 1;
@@ -578,14 +600,25 @@ __global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
     }
   };
 
+  // The first batch of weights (row set 0) is requested as soon as the route record is in
+  // LDS; the activations are staged while those loads are in flight.
+  DownW w0[kNB];
+  if (ni > 0) load_down(4 * HG * (int)blockIdx.x + grp, 0, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (A_LDS) {
+    stage_pieces<(TC == 1 ? 4 : 8), 256>(reinterpret_cast<uint4*>(as), reinterpret_cast<const uint4*>(p.b.a),
+                    (int)(a_elems / 8));
+    __syncthreads();
+  }
+
   // batches of kNB entries, the next batch requested before the current one is used
 #pragma unroll
   for (int r = 0; r < HG; ++r) {
     const int h = 4 * (HG * (int)blockIdx.x + r) + grp;
     float acc = 0.0f;
     if (ni > 0) {
-      DownW w0[kNB], w1[kNB];
-      load_down(h, 0, w0);
+      DownW w1[kNB];
+      if (r > 0) load_down(h, 0, w0);
       __builtin_amdgcn_sched_barrier(0);
       for (int i0 = 0; i0 < ni; i0 += 2 * kNB) {
         if (i0 + kNB < ni) load_down(h, i0 + kNB, w1);
@@ -670,13 +703,14 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const bool a_lds = a_bytes + lds_c_route <= kDecLdsMax;
   const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
   const int nA = d.E + (d.Fs > 0 ? 1 + d.Fs : 0);
-  const dim3 gA((nA + 3) / 4), gB(4 * device_cus()), gC(d.H / (4 * HG)), blk(256);
+  const dim3 gA((nA + 3) / 4), gB(device_cus() * 4 / (kDecBWaves / 4)), gC(d.H / (4 * HG)), blk(256);
+  const dim3 blkB(64 * kDecBWaves);
 #define MOE_DEC(TCV, NJV)                                                        \
   do {                                                                           \
     if (phase < 0 || phase == 0)                                                 \
       hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x, s, p);                  \
     if (phase < 0 || phase == 1)                                                 \
-      hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blk, lds_b, s, p);             \
+      hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blkB, lds_b, s, p);            \
     if (phase < 0 || phase == 2) {                                               \
       constexpr int HGV = HG;                                                    \
       if (a_lds)                                                                 \

@@ -224,47 +224,70 @@ __device__ __forceinline__ float key_value(int k) {
 }
 
 // Top-k of one token's E logits by one wave (E <= 64*NJ) with the softmax over the selected
-// logits. Lane l holds logits e = NJ*l + j in v[j] (consecutive experts per lane). Each of the
-// K rounds takes the wave maximum M of the remaining order keys; the winner is the lowest
-// expert index whose key equals M: the lowest lane holding one (one ballot), then the lowest
-// j in that lane. Lane r < K ends with the rank-r expert my_i, its logit my_v and its
-// renormalised weight my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank
-// order; lanes >= K get my_w = 0.
+// logits. Lane l holds logits e = NJ*l + j in v[j] (consecutive experts per lane). The order
+// (larger logit first, lower expert index first among equal logits) is a total order, so the
+// selection is unique:
+//   1. each lane sorts its NJ (key, index) pairs by that order once (odd-even transposition on
+//      64-bit composites, so equal keys keep ascending indices);
+//   2. each of the K rounds takes the wave maximum M of the lanes' heads; the winner is the
+//      lowest lane whose head equals M (a lower lane holds only lower indices), read with one
+//      ballot; that lane drops its head.
+// Lane r < K ends with the rank-r expert my_i, its logit my_v and its renormalised weight
+// my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank order; lanes >= K get
+// my_w = 0.
 template <int NJ>
 __device__ __forceinline__ void wave_topk_softmax(const float (&v)[NJ], int E, int K, int lane,
                                                   float& my_v, int& my_i, float& my_w) {
-  int key[NJ];
+  // composite: order key (sign flipped to unsigned order) above the complemented index, so a
+  // larger composite is earlier in the order
+  uint64_t c[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) key[j] = NJ * lane + j < E ? order_key(v[j]) : INT_MIN;
-  my_v = -INFINITY;
-  my_i = 0;
-  float my_z = 0.0f, m0 = 0.0f, den = 0.0f;
-  for (int r = 0; r < K; ++r) {
-    int lm = key[0];
+  for (int j = 0; j < NJ; ++j) {
+    const int e = NJ * lane + j;
+    const int key = e < E ? order_key(v[j]) : INT_MIN;
+    c[j] = ((uint64_t)((uint32_t)key ^ 0x80000000u) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+  }
 #pragma unroll
-    for (int j = 1; j < NJ; ++j) lm = max(lm, key[j]);
-    const int M = wave_max_i32(lm);
-    int jf = NJ;  // first j of this lane holding M
+  for (int pass = 0; pass < NJ; ++pass) {
 #pragma unroll
-    for (int j = NJ - 1; j >= 0; --j)
-      if (key[j] == M) jf = j;
-    const uint64_t b = __ballot(jf < NJ);
-    const int L = (int)__builtin_ctzll(b);
-    const int jL = __builtin_amdgcn_readlane(jf, L);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (lane == L && j == jL) key[j] = INT_MIN;
-    const float Mf = key_value(M);
-    if (r == 0) m0 = Mf;
-    const float z = __expf(Mf - m0);
-    den += z;
-    if (lane == r) {
-      my_v = Mf;
-      my_i = NJ * L + jL;
-      my_z = z;
+    for (int j = pass & 1; j + 1 < NJ; j += 2) {
+      const uint64_t a = c[j], b = c[j + 1];
+      const bool sw = b > a;
+      c[j] = sw ? b : a;
+      c[j + 1] = sw ? a : b;
     }
   }
-  my_w = lane < K ? my_z / den : 0.0f;
+  int key[NJ], idx[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    key[j] = (int)((uint32_t)(c[j] >> 32) ^ 0x80000000u);
+    idx[j] = (int)(0xFFFFFFFFu - (uint32_t)c[j]);
+  }
+  int sel_key = INT_MIN, sel_idx = 0;
+  for (int r = 0; r < K; ++r) {
+    const int M = wave_max_i32(key[0]);
+    const int L = (int)__builtin_ctzll(__ballot(key[0] == M));
+    const int I = __builtin_amdgcn_readlane(idx[0], L);
+    if (lane == L) {
+#pragma unroll
+      for (int j = 0; j + 1 < NJ; ++j) {
+        key[j] = key[j + 1];
+        idx[j] = idx[j + 1];
+      }
+      key[NJ - 1] = INT_MIN;
+    }
+    if (lane == r) {
+      sel_key = M;
+      sel_idx = I;
+    }
+  }
+  my_v = lane < K ? key_value(sel_key) : -INFINITY;
+  my_i = sel_idx;
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+  const float z = lane < K ? __expf(my_v - m0) : 0.0f;
+  float den = 0.0f;
+  for (int r = 0; r < K; ++r) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), r));
+  my_w = lane < K ? z / den : 0.0f;
 }
 
 // Lane l takes logits NJ*l .. NJ*l + NJ - 1 (-inf past E).
