@@ -22,10 +22,10 @@
 //     registers and store A = bf16(silu(G) * U); workgroup 0 also stores the per-expert route
 //     record for C;
 //   C (k_dec_c): down projection fused with the weighted combine of the bf16-rounded expert
-//     outputs. The route record and the activations are staged in LDS; each 16-lane group
-//     owns output rows, the four waves of a workgroup walk interleaved quarters of the entry
-//     list (the shared expert last), and their partial sums are added in LDS in a fixed
-//     order, so the result is deterministic.
+//     outputs. A workgroup owns four output rows (one per 16-lane group) and has one wave
+//     per entry (the selected experts, the shared expert last; at most 16 waves, which then
+//     take several entries each); the waves' partial sums are added in LDS in wave order,
+//     so the result is deterministic.
 // Every selected weight byte is read from HBM once per call.
 #include "moe_internal.h"
 
@@ -37,6 +37,9 @@ constexpr int kNB = 4;  // down rows requested per batch by one 16-lane group
 // k_dec_b runs one 16-wave workgroup per CU: a single wave per CU derives the top-k, so the
 // selection rounds of different workgroups do not share a SIMD's issue slots.
 constexpr int kDecBWaves = 16;
+// k_dec_c: output rows per 16-lane group (two for a single token, whose waves have one entry
+// each; one for larger batches, whose waves keep several entries in flight)
+__host__ __device__ constexpr int dec_c_rows(int tc) { return tc == 1 ? 2 : 1; }
 }  // namespace
 
 struct DecodeArgs {
@@ -240,21 +243,22 @@ __device__ void build_route(const Route& R, const int* sel_idx, const float* sel
   __syncthreads();
 }
 
-// Copy n 16-byte pieces from global memory to LDS with the NT threads of the workgroup, NB
+// Copy n 16-byte pieces from global memory to LDS with the nt threads of the workgroup, NB
 // pieces per thread in flight: each batch issues all its loads (indices past the end re-read
 // the last piece) before the first LDS write, so a batch costs one memory round trip.
-template <int NB, int NT>
-__device__ __forceinline__ void stage_pieces(uint4* dst, const uint4* __restrict__ src, int n) {
-  for (int v0 = threadIdx.x; v0 < n; v0 += NB * NT) {
+template <int NB>
+__device__ __forceinline__ void stage_pieces(uint4* dst, const uint4* __restrict__ src, int n,
+                                             int nt) {
+  for (int v0 = threadIdx.x; v0 < n; v0 += NB * nt) {
     uint4 t[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int v = v0 + b * NT;
+      const int v = v0 + b * nt;
       t[b] = src[v < n ? v : n - 1];
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int v = v0 + b * NT;
+      const int v = v0 + b * nt;
       if (v < n) dst[v] = t[b];
     }
   }
@@ -264,8 +268,8 @@ __device__ __forceinline__ void stage_pieces(uint4* dst, const uint4* __restrict
 template <int TC, int NT>
 __device__ __forceinline__ void stage_x(uint16_t* xs, const uint16_t* __restrict__ x, int n8) {
   constexpr int per = (TC * 256 + NT - 1) / NT;
-  stage_pieces<(per < 8 ? per : 8), NT>(reinterpret_cast<uint4*>(xs),
-                                        reinterpret_cast<const uint4*>(x), n8);
+  stage_pieces<(per < 8 ? per : 8)>(reinterpret_cast<uint4*>(xs),
+                                    reinterpret_cast<const uint4*>(x), n8, NT);
 }
 
 // ============================================================================ A
@@ -475,171 +479,205 @@ struct DownW {
   uint16_t s, b;  // raw bf16 bits (16-bit for the same reason as in PairW)
 };
 
-// A workgroup owns 4*HG consecutive output rows: 16-lane group g of every wave takes rows
-// h = 4*(HG*blockIdx.x + r) + g, r < HG. Wave w walks the entries d = w, w + 4, ... (ascending
-// expert id, the shared expert last), so the four groups of a wave read the same activation
-// chunks. Each lane sl of a group accumulates the weighted sum for token sl; the four waves'
-// sums are added in LDS in a fixed order, so the result is deterministic.
-// A_LDS: the activations of the call are staged in LDS (when they fit) instead of being read
-// from global memory for every entry.
-template <int TC, int HG, bool A_LDS>
-__global__ __launch_bounds__(256) void k_dec_c(DecodeArgs p) {
+// A workgroup of NW waves (blockDim.x = 64*NW, NW <= 16) owns the 4*kRG output rows
+// h = 4*(kRG*blockIdx.x + r) + g, r < kRG: 16-lane group g of every wave takes kRG rows
+// (one workgroup per CU for the full-size layer, all resident at once). Wave w walks the entries
+// d = w, w + NW, ... (ascending expert id, the shared expert last); lane sl of a group
+// accumulates, for token sl, the routing-weighted bf16-rounded expert outputs of the wave's
+// entries. The waves' sums are then added in LDS in wave order, so the result is deterministic.
+// The launcher sizes NW to the number of entries (at most 16): for a single token every wave
+// has exactly one entry, and each lane's 32 activations of that entry are requested from
+// global memory together with its weights (the four groups of a wave read the same
+// addresses). Larger batches stage the activations in LDS when they fit (A_LDS).
+template <int TC, bool A_LDS>
+__global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint4 smem[];
-  const int T = p.T, H = p.H, K = p.K, F = p.F, Fs = p.Fs, TK = T * K;
+  constexpr int kRG = dec_c_rows(TC);
+  const int T = p.T, H = p.H, F = p.F, Fs = p.Fs, TK = T * p.K;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int NW = __builtin_amdgcn_readfirstlane((int)blockDim.x >> 6);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int sl = lane & 15, grp = lane >> 4;
+  const int h0 = 4 * kRG * (int)blockIdx.x + grp;  // row r of the group: h0 + 4*r
   const size_t a_elems = (size_t)TK * F + (size_t)T * Fs;
   uint16_t* as = reinterpret_cast<uint16_t*>(smem);                       // [a_elems] if A_LDS
-  float* part = reinterpret_cast<float*>(A_LDS ? (void*)(as + a_elems) : (void*)smem);
-  const Route R = carve_route(part + 4 * HG * 64, TK, T);                 // part: [4][HG][64]
+  float* part = reinterpret_cast<float*>(A_LDS ? (void*)(as + a_elems) : (void*)smem);  // [NW][kRG][64]
+  const Route R = carve_route(part + 64 * kRG * NW, TK, T);
 
   const int nw = (int)route_words(TK, T);
-  for (int i = tid; i < nw; i += 256) R.nd[i] = p.b.route[i];
+  for (int i = tid; i < nw; i += (int)blockDim.x) R.nd[i] = p.b.route[i];
   __syncthreads();
   const int D = *R.nd;
   const int nD = D + (Fs > 0 ? 1 : 0);  // the shared expert is the last entry
-  const int ni = wave < nD ? (nD - wave + 3) >> 2 : 0;  // entries of this wave
+  const int ni = wave < nD ? (nD - wave + NW - 1) / NW : 0;  // entries of this wave
   const uint16_t* abase = A_LDS ? as : p.b.a;
 
-  // Entries i0 .. i0+kNB-1 of this wave for row h; none past the wave's list is requested.
-  // Lanes past a short row re-read its last chunk (never used), so the loads of an entry are
-  // unconditional; the weight pointers are selected as values, not as references into the
-  // argument block (which would be read with vector loads and waited for).
+  // Entries i0 .. i0+kB-1 of this wave; none past the wave's list is requested. Lanes past a
+  // short row re-read its last chunk (never used), so the loads of an entry are unconditional;
+  // the weight pointers are selected as values, not as references into the argument block
+  // (which would be read with vector loads and waited for).
+  constexpr int kB = TC == 1 ? 1 : kNB;  // entries per batch
   const uint32_t* const rq = p.down.q;
   const uint16_t* const rs = p.down.scale;
   const uint16_t* const rb = p.down.bias;
   const uint32_t* const sq = p.sh_down.q;
   const uint16_t* const ss = p.sh_down.scale;
   const uint16_t* const sb = p.sh_down.bias;
-  auto load_down = [&](int h, int i0, DownW (&dw)[kNB]) {
+  struct Batch {
+    DownW w[kB][kRG];
+    uint4 a[TC == 1 ? kB : 1][4];  // single token: the lane's 32 activations of the entry
+  };
+  auto load_down = [&](int i0, Batch& bt) {
 #pragma unroll
-    for (int b = 0; b < kNB; ++b) {
-      const int d = wave + 4 * (i0 + b);
-      if (d >= nD) break;  // uniform over the wave: no request past the wave's last entry
+    for (int b = 0; b < kB; ++b) {
+      const int d = wave + NW * (i0 + b);
+      if (d >= nD) break;  // uniform over the wave
       const bool sh = d == D;
       const int Kd = sh ? Fs : F;
       const int c = sl < (Kd >> 5) ? sl : (Kd >> 5) - 1;
-      const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
       const uint32_t* q = sh ? sq : rq;
       const uint16_t* sp = sh ? ss : rs;
       const uint16_t* bp = sh ? sb : rb;
-      const size_t g = row * (size_t)(Kd >> 6) + (c >> 1);
-      dw[b].q = reinterpret_cast<const uint4*>(q + row * (size_t)(Kd >> 3))[c];
-      dw[b].s = sp[g];
-      dw[b].b = bp[g];
+#pragma unroll
+      for (int r = 0; r < kRG; ++r) {
+        const int h = h0 + 4 * r;
+        const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
+        const size_t g = row * (size_t)(Kd >> 6) + (c >> 1);
+        bt.w[b][r].q = reinterpret_cast<const uint4*>(q + row * (size_t)(Kd >> 3))[c];
+        bt.w[b][r].s = sp[g];
+        bt.w[b][r].b = bp[g];
+      }
+      if constexpr (TC == 1) {
+        const uint16_t* ar = sh ? p.b.a + (size_t)TK * F : p.b.a + (size_t)R.ent_row0[d] * F;
+        const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bt.a[b][k] = av[k];
+      }
     }
   };
-  auto use_down = [&](int i0, const DownW (&dw)[kNB], float& acc) {
+  auto use_down = [&](int i0, const Batch& bt, float (&accr)[kRG]) {
 #pragma unroll
-    for (int b = 0; b < kNB; ++b) {
+    for (int b = 0; b < kB; ++b) {
       if (i0 + b >= ni) break;  // uniform over the wave
-      const int d = wave + 4 * (i0 + b);
+      const int d = wave + NW * (i0 + b);
       const bool sh = d == D;
       const int Kd = sh ? Fs : F;
-      const int m = __builtin_amdgcn_readfirstlane(sh ? T : R.ent_m[d]);
       const int row0 = sh ? 0 : R.ent_row0[d];
-      const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
-      uint32_t wd[16];
-      const float ds = bf16_to_f32(dw[b].s), db = bf16_to_f32(dw[b].b);
-      dequant8(dw[b].q.x, ds, db, wd + 0);
-      dequant8(dw[b].q.y, ds, db, wd + 4);
-      dequant8(dw[b].q.z, ds, db, wd + 8);
-      dequant8(dw[b].q.w, ds, db, wd + 12);
-      if (TC > 1 && m == 1) {
-        // one token (bit t of the mask): every lane of the group ends with the row's sum
-        float one[1] = {0.0f};
-        if (sl < (Kd >> 5)) {
-          const uint4* av = reinterpret_cast<const uint4*>(abase + (size_t)row0 * F + 32 * sl);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 a4 = av[q];
-            one[0] = dot2_bf16(a4.x, wd[4 * q + 0], one[0]);
-            one[0] = dot2_bf16(a4.y, wd[4 * q + 1], one[0]);
-            one[0] = dot2_bf16(a4.z, wd[4 * q + 2], one[0]);
-            one[0] = dot2_bf16(a4.w, wd[4 * q + 3], one[0]);
+      for (int r = 0; r < kRG; ++r) {
+        float& acc = accr[r];
+        uint32_t wd[16];
+        const float ds = bf16_to_f32(bt.w[b][r].s), db = bf16_to_f32(bt.w[b][r].b);
+        dequant8(bt.w[b][r].q.x, ds, db, wd + 0);
+        dequant8(bt.w[b][r].q.y, ds, db, wd + 4);
+        dequant8(bt.w[b][r].q.z, ds, db, wd + 8);
+        dequant8(bt.w[b][r].q.w, ds, db, wd + 12);
+        if constexpr (TC == 1) {
+          float one[1] = {0.0f};
+          if (sl < (Kd >> 5)) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              one[0] = dot2_bf16(bt.a[b][k].x, wd[4 * k + 0], one[0]);
+              one[0] = dot2_bf16(bt.a[b][k].y, wd[4 * k + 1], one[0]);
+              one[0] = dot2_bf16(bt.a[b][k].z, wd[4 * k + 2], one[0]);
+              one[0] = dot2_bf16(bt.a[b][k].w, wd[4 * k + 3], one[0]);
+            }
           }
-        }
-        group_reduce<1, 16>(one, sl);
-        if (sl < T && ((tmask >> sl) & 1u))
-          acc = __builtin_fmaf(R.row_w[row0], round_bf16(one[0]), acc);
-        continue;
-      }
-      float dots[TC];
+          group_reduce<1, 16>(one, sl);
+          const float wgt = sh ? R.sgs[0] : R.row_w[row0];
+          if (sl == 0) acc = __builtin_fmaf(wgt, round_bf16(one[0]), acc);  // bf16 expert output
+          continue;
+        } else {
+          const int m = __builtin_amdgcn_readfirstlane(sh ? T : R.ent_m[d]);
+          const unsigned tmask = sh ? 0xFFFFFFFFu : R.ent_mask[d];
+          if (m == 1) {
+            // one token (bit t of the mask): every lane of the group ends with the row's sum
+            float one[1] = {0.0f};
+            if (sl < (Kd >> 5)) {
+              const uint4* av = reinterpret_cast<const uint4*>(abase + (size_t)row0 * F + 32 * sl);
 #pragma unroll
-      for (int j = 0; j < TC; ++j) {
-        dots[j] = 0.0f;
-        if (j < m && sl < (Kd >> 5)) {
-          const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
-                                  : abase + (size_t)(row0 + j) * F;
-          const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
-          float s = 0.0f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 a4 = av[q];
-            s = dot2_bf16(a4.x, wd[4 * q + 0], s);
-            s = dot2_bf16(a4.y, wd[4 * q + 1], s);
-            s = dot2_bf16(a4.z, wd[4 * q + 2], s);
-            s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+              for (int q = 0; q < 4; ++q) {
+                const uint4 a4 = av[q];
+                one[0] = dot2_bf16(a4.x, wd[4 * q + 0], one[0]);
+                one[0] = dot2_bf16(a4.y, wd[4 * q + 1], one[0]);
+                one[0] = dot2_bf16(a4.z, wd[4 * q + 2], one[0]);
+                one[0] = dot2_bf16(a4.w, wd[4 * q + 3], one[0]);
+              }
+            }
+            group_reduce<1, 16>(one, sl);
+            if (sl < T && ((tmask >> sl) & 1u))
+              acc = __builtin_fmaf(R.row_w[row0], round_bf16(one[0]), acc);
+            continue;
           }
-          dots[j] = s;
+          float dots[TC];
+#pragma unroll
+          for (int j = 0; j < TC; ++j) {
+            dots[j] = 0.0f;
+            if (j < m && sl < (Kd >> 5)) {
+              const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
+                                      : abase + (size_t)(row0 + j) * F;
+              const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
+              float s = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint4 a4 = av[q];
+                s = dot2_bf16(a4.x, wd[4 * q + 0], s);
+                s = dot2_bf16(a4.y, wd[4 * q + 1], s);
+                s = dot2_bf16(a4.z, wd[4 * q + 2], s);
+                s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+              }
+              dots[j] = s;
+            }
+          }
+          group_reduce<TC, 16>(dots, sl);
+          // lane sl (= token) takes its entry: the token's rank inside this expert
+          int j = 0;
+          bool mine = false;
+          float wgt = 0.0f;
+          if (sl < T && ((tmask >> sl) & 1u)) {
+            j = __popc(tmask & ((1u << sl) - 1u));
+            mine = true;
+            wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
+          }
+          const float val = __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
+          if (mine) acc = __builtin_fmaf(wgt, round_bf16(val), acc);  // the expert output in bf16
         }
       }
-      group_reduce<TC, 16>(dots, sl);
-      // lane sl (= token) takes its entry: the token's rank inside this expert
-      int j = 0;
-      bool mine = false;
-      float wgt = 0.0f;
-      if (sl < T && ((tmask >> sl) & 1u)) {
-        j = __popc(tmask & ((1u << sl) - 1u));
-        mine = true;
-        wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
-      }
-      const float val = TC == 1 ? dots[0] : __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
-      if (mine) acc = __builtin_fmaf(wgt, round_bf16(val), acc);  // the expert output in bf16
     }
   };
 
-  // The first batch of weights (row set 0) is requested as soon as the route record is in
-  // LDS; the activations are staged while those loads are in flight.
-  DownW w0[kNB];
-  if (ni > 0) load_down(4 * HG * (int)blockIdx.x + grp, 0, w0);
+  // The first batch is requested as soon as the route record is in LDS; the activations are
+  // staged (A_LDS) while those loads are in flight.
+  float acc[kRG];
+#pragma unroll
+  for (int r = 0; r < kRG; ++r) acc[r] = 0.0f;
+  Batch b0, b1;
+  if (ni > 0) load_down(0, b0);
   __builtin_amdgcn_sched_barrier(0);
   if (A_LDS) {
-    stage_pieces<(TC == 1 ? 4 : 8), 256>(reinterpret_cast<uint4*>(as), reinterpret_cast<const uint4*>(p.b.a),
-                    (int)(a_elems / 8));
+    stage_pieces<8>(reinterpret_cast<uint4*>(as), reinterpret_cast<const uint4*>(p.b.a),
+                    (int)(a_elems / 8), (int)blockDim.x);
     __syncthreads();
   }
-
-  // batches of kNB entries, the next batch requested before the current one is used
-#pragma unroll
-  for (int r = 0; r < HG; ++r) {
-    const int h = 4 * (HG * (int)blockIdx.x + r) + grp;
-    float acc = 0.0f;
-    if (ni > 0) {
-      DownW w1[kNB];
-      if (r > 0) load_down(h, 0, w0);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int i0 = 0; i0 < ni; i0 += 2 * kNB) {
-        if (i0 + kNB < ni) load_down(h, i0 + kNB, w1);
-        __builtin_amdgcn_sched_barrier(0);
-        use_down(i0, w0, acc);
-        if (i0 + kNB >= ni) break;
-        if (i0 + 2 * kNB < ni) load_down(h, i0 + 2 * kNB, w0);
-        __builtin_amdgcn_sched_barrier(0);
-        use_down(i0 + kNB, w1, acc);
-      }
-    }
-    part[(wave * HG + r) * 64 + lane] = acc;
+  // batches of kB entries, the next batch requested before the current one is used
+  for (int i0 = 0; i0 < ni; i0 += 2 * kB) {
+    if (i0 + kB < ni) load_down(i0 + kB, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    use_down(i0, b0, acc);
+    if (i0 + kB >= ni) break;
+    if (i0 + 2 * kB < ni) load_down(i0 + 2 * kB, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    use_down(i0 + kB, b1, acc);
   }
+#pragma unroll
+  for (int r = 0; r < kRG; ++r) part[(wave * kRG + r) * 64 + lane] = acc[r];
   __syncthreads();
-  // wave w writes rows r = w, w + 4, ... of the workgroup's HG row sets
-  for (int r = wave; r < HG; r += 4) {
-    const int h = 4 * (HG * (int)blockIdx.x + r) + grp;
+  // waves r, r + NW, ... add row r's partial sums over the waves in wave order
+  for (int r = wave; r < kRG; r += NW) {
     if (sl < T) {
-      const float v = ((part[(0 * HG + r) * 64 + lane] + part[(1 * HG + r) * 64 + lane]) +
-                       part[(2 * HG + r) * 64 + lane]) + part[(3 * HG + r) * 64 + lane];
-      p.out[(size_t)sl * H + h] = v;
+      float v = part[r * 64 + lane];
+      for (int w = 1; w < NW; ++w) v += part[(w * kRG + r) * 64 + lane];
+      p.out[(size_t)sl * H + h0 + 4 * r] = v;
     }
   }
 }
@@ -698,13 +736,16 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const size_t lds_x = (size_t)d.T * d.H * 2;
   const size_t lds_b = lds_x + decode_b_lds_words(d) * 4;
   const size_t a_bytes = ((size_t)d.TK() * d.F + (size_t)d.T * d.Fs) * 2;
-  constexpr int HG = 1;  // output rows per 16-lane group
-  const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4 + (size_t)4 * HG * 64 * 4;
-  const bool a_lds = a_bytes + lds_c_route <= kDecLdsMax;
+  // C: one wave per entry (the selected experts and the shared one), at most 16 waves
+  const int ent_max = d.TK() + (d.Fs > 0 ? 1 : 0);
+  const int nwc = ent_max < 16 ? ent_max : 16;
+  const int rgc = dec_c_rows(d.T <= 1 ? 1 : 2);
+  const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4 + (size_t)nwc * rgc * 64 * 4;
+  const bool a_lds = d.T > 1 && a_bytes + lds_c_route <= kDecLdsMax;
   const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
   const int nA = d.E + (d.Fs > 0 ? 1 + d.Fs : 0);
-  const dim3 gA((nA + 3) / 4), gB(device_cus() * 4 / (kDecBWaves / 4)), gC(d.H / (4 * HG)), blk(256);
-  const dim3 blkB(64 * kDecBWaves);
+  const dim3 gA((nA + 3) / 4), gB(device_cus() * 4 / (kDecBWaves / 4)), gC(d.H / (4 * rgc)), blk(256);
+  const dim3 blkB(64 * kDecBWaves), blkC(64 * nwc);
 #define MOE_DEC(TCV, NJV)                                                        \
   do {                                                                           \
     if (phase < 0 || phase == 0)                                                 \
@@ -712,11 +753,10 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
     if (phase < 0 || phase == 1)                                                 \
       hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blkB, lds_b, s, p);            \
     if (phase < 0 || phase == 2) {                                               \
-      constexpr int HGV = HG;                                                    \
       if (a_lds)                                                                 \
-        hipLaunchKernelGGL((k_dec_c<TCV, HGV, true>), gC, blk, lds_c, s, p);     \
+        hipLaunchKernelGGL((k_dec_c<TCV, true>), gC, blkC, lds_c, s, p);         \
       else                                                                       \
-        hipLaunchKernelGGL((k_dec_c<TCV, HGV, false>), gC, blk, lds_c, s, p);    \
+        hipLaunchKernelGGL((k_dec_c<TCV, false>), gC, blkC, lds_c, s, p);        \
     }                                                                            \
   } while (0)
 #define MOE_DEC_T(NJV) \

@@ -25,6 +25,7 @@ CASES = [
     ("mid", 300, ATOMIC),
     ("full", 1, 0), ("full", 8, 0), ("full", 16, 0), ("full", 8, FORCE),
     ("wide", 1, 0), ("wide", 4, 0), ("wide", 40, 0),
+    ("solo", 1, 0), ("solo", 5, 0), ("solo", 40, 0),
 ]
 
 
