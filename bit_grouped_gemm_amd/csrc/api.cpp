@@ -448,6 +448,26 @@ int moe_stack_forward(const moe_layer_desc_t* const* layers, int32_t n_layers, f
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_residual_rmsnorm(nullptr, resid, x, T, H, eps, 1, s) != hipSuccess)
     return MOE_HIP_ERROR;
+  // Decode-sized batches: three launches per layer, the residual update and the RMSNorm folded
+  // into the layer's first and last kernels (same arithmetic, same bits), then one final
+  // normalisation of the last residual.
+  bool fused = true;
+  for (int l = 0; l < n_layers && fused; ++l) {
+    const Dims d = dims_of(layers[l], T);
+    fused = use_decode(d, flags) && decode_fast_ok(d);
+  }
+  if (fused) {
+    const StackFuse sf{resid, x, eps};
+    for (int l = 0; l < n_layers; ++l) {
+      const Dims d = dims_of(layers[l], T);
+      const Layout L = layout_of(d, flags);
+      const DecodeBufs b{at<float>(workspace, L.logits), at<int32_t>(workspace, L.droute),
+                         at<uint16_t>(workspace, L.a)};
+      if (launch_decode_layer(d, *layers[l], nullptr, b, nullptr, s, -1, &sf) != hipSuccess)
+        return MOE_HIP_ERROR;
+    }
+    return hip_status(launch_residual_rmsnorm(nullptr, resid, x, T, H, eps, 2, s));
+  }
   for (int l = 0; l < n_layers; ++l) {
     int st = moe_layer_forward(layers[l], x, T, y, workspace, lws, flags, stream);
     if (st != MOE_OK) return st;

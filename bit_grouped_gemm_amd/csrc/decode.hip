@@ -51,6 +51,12 @@ struct DecodeArgs {
   int T, H, E, K, F, Fs;
   DecodeBufs b;
   float* out;       // [T, H]
+  // inside the stack: A derives x from the residual stream rin (workgroup 0 writes it to xw),
+  // and C adds the layer output into out (= the residual stream) instead of storing it
+  const float* rin;
+  uint16_t* xw;
+  float eps;
+  int acc_out;
 };
 
 // Butterfly sum of v[0..N) over aligned groups of W lanes (W = 16 or 64, N a power of two).
@@ -264,6 +270,48 @@ __device__ __forceinline__ void stage_pieces(uint4* dst, const uint4* __restrict
   }
 }
 
+// x = bf16(RMSNorm(r)) of T <= TC tokens (H <= 2048), by the 256 threads of the workgroup, into
+// xs and, if xw is not null, to global memory: the same loads, fused multiply-adds, wave
+// reduction, combination of the four wave sums, correctly rounded division and square root and
+// bf16 rounding as k_residual_rmsnorm, so both give the same bits. part: 4 floats of LDS.
+__device__ __forceinline__ void norm_x(uint16_t* xs, const float* __restrict__ r, int T, int H,
+                                       float eps, uint16_t* xw, float* part) {
+  const int tid = threadIdx.x;
+  for (int t = 0; t < T; ++t) {
+    const float* rr = r + (size_t)t * H;
+    float4 v[2];
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 4 * tid + 1024 * k;
+      if (i < H) {
+        v[k] = *reinterpret_cast<const float4*>(rr + i);
+        ss = __builtin_fmaf(v[k].x, v[k].x, ss);
+        ss = __builtin_fmaf(v[k].y, v[k].y, ss);
+        ss = __builtin_fmaf(v[k].z, v[k].z, ss);
+        ss = __builtin_fmaf(v[k].w, v[k].w, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float den = sqrtf(tot / (float)H + eps);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 4 * tid + 1024 * k;
+      if (i < H) {
+        uint2 o;
+        o.x = pack_bf16x2(v[k].x / den, v[k].y / den);
+        o.y = pack_bf16x2(v[k].z / den, v[k].w / den);
+        *reinterpret_cast<uint2*>(xs + (size_t)t * H + i) = o;
+        if (xw) *reinterpret_cast<uint2*>(xw + (size_t)t * H + i) = o;
+      }
+    }
+    __syncthreads();  // part is reused by the next token
+  }
+}
+
 // x of up to TC tokens with NT threads (H <= 2048: at most TC*256/NT pieces per thread)
 template <int TC, int NT>
 __device__ __forceinline__ void stage_x(uint16_t* xs, const uint16_t* __restrict__ x, int n8) {
@@ -302,8 +350,14 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
   } else if (shared_task) {
     load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
   }
-  stage_x<TC, 256>(xs, p.x, (T * H) >> 3);
-  __syncthreads();
+  if (p.rin) {
+    // inside the stack: x from the residual stream (workgroup 0 also writes it for B)
+    float* part = reinterpret_cast<float*>(xs + (size_t)T * H);
+    norm_x(xs, p.rin, T, H, p.eps, blockIdx.x == 0 ? p.xw : nullptr, part);
+  } else {
+    stage_x<TC, 256>(xs, p.x, (T * H) >> 3);
+    __syncthreads();
+  }
 
   if (router) {
     float acc[TC];
@@ -677,7 +731,8 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
     if (sl < T) {
       float v = part[r * 64 + lane];
       for (int w = 1; w < NW; ++w) v += part[(w * kRG + r) * 64 + lane];
-      p.out[(size_t)sl * H + h0 + 4 * r] = v;
+      float* o = p.out + (size_t)sl * H + h0 + 4 * r;
+      *o = p.acc_out ? *o + v : v;  // inside the stack: the residual update r + y
     }
   }
 }
@@ -713,9 +768,15 @@ bool decode_fast_ok(const Dims& d) {
 }
 
 hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
-                               const DecodeBufs& b, float* out, hipStream_t s, int phase) {
+                               const DecodeBufs& b, float* out, hipStream_t s, int phase,
+                               const StackFuse* sf) {
   DecodeArgs p;
-  p.x = x;
+  p.x = sf ? sf->x : x;
+  p.rin = sf ? sf->resid : nullptr;
+  p.xw = sf ? sf->x : nullptr;
+  p.eps = sf ? sf->eps : 0.0f;
+  p.acc_out = sf ? 1 : 0;
+  if (sf) out = sf->resid;
   p.router_w = desc.router_w;
   p.router_bias = desc.router_bias;
   p.wg = d.Fs > 0 ? desc.shared_gate_w : nullptr;
@@ -749,7 +810,7 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
 #define MOE_DEC(TCV, NJV)                                                        \
   do {                                                                           \
     if (phase < 0 || phase == 0)                                                 \
-      hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x, s, p);                  \
+      hipLaunchKernelGGL((k_dec_a<TCV>), gA, blk, lds_x + 16, s, p);             \
     if (phase < 0 || phase == 1)                                                 \
       hipLaunchKernelGGL((k_dec_b<TCV, NJV>), gB, blkB, lds_b, s, p);            \
     if (phase < 0 || phase == 2) {                                               \

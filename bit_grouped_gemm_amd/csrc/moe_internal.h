@@ -80,9 +80,20 @@ struct DecodeBufs {
 };
 bool decode_fast_ok(const Dims& d);
 size_t decode_route_bytes(const Dims& d);
-// phase < 0: all three launches; 0, 1, 2: only that one.
+// A decode layer inside the stack (moe_stack_forward): the first kernel derives the layer input
+// x = bf16(RMSNorm(resid)) itself (bit for bit as k_residual_rmsnorm does) and writes it to x,
+// and the last kernel adds the layer output into resid in place.
+struct StackFuse {
+  float* resid;  // [T, H] fp32 residual stream
+  uint16_t* x;   // [T, H] bf16: written by the first kernel, read by the second
+  float eps;
+};
+// phase < 0: all three launches; 0, 1, 2: only that one. sf == nullptr: a plain layer call
+// (x in, out = the layer output); otherwise x and out are ignored and sf is used.
 hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
-                               const DecodeBufs& b, float* out, hipStream_t s, int phase);
+                               const DecodeBufs& b, float* out, hipStream_t s, int phase,
+                               const StackFuse* sf = nullptr);
+// init: 0 r <- r + y, 1 r <- x (as fp32), 2 r unchanged; then x <- bf16(RMSNorm(r)).
 hipError_t launch_residual_rmsnorm(const float* y, float* r, uint16_t* x, int T, int H, float eps,
                                    int init, hipStream_t s);
 hipError_t launch_debug_dequant(const moe_w4_t& w, int n_rows, int kin, int mat, int row,

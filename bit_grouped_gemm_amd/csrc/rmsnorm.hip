@@ -7,8 +7,9 @@
 // round trip. Between two MoE layers the fp32 residual stream takes the layer output and the
 // next layer reads its RMS-normalised bf16 copy:
 //   r <- r + y,   x <- bf16( r / sqrt(mean(r^2) + eps) )      (unit weight)
-// (init: r <- x as fp32, then the same normalisation). One workgroup per token row; the row is
-// read once, its sum of squares reduced in the workgroup, then written normalised.
+// (init 1: r <- x as fp32, then the same normalisation; init 2: r unchanged, normalisation only).
+// One workgroup per token row; the row is read once, its sum of squares reduced in the
+// workgroup, then written normalised.
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,16 +25,18 @@ __global__ __launch_bounds__(256) void k_residual_rmsnorm(const float* __restric
   float ss = 0.0f;
   for (int i = 4 * tid; i < H; i += 1024) {
     float4 v;
-    if (init) {
+    if (init == 1) {
       const uint2 b = *reinterpret_cast<const uint2*>(xx + i);
       v = make_float4(bf16_to_f32(b.x & 0xFFFFu), bf16_to_f32(b.x >> 16),
                       bf16_to_f32(b.y & 0xFFFFu), bf16_to_f32(b.y >> 16));
+    } else if (init == 2) {
+      v = *reinterpret_cast<const float4*>(rr + i);
     } else {
       const float4 a = *reinterpret_cast<const float4*>(rr + i);
       const float4 u = *reinterpret_cast<const float4*>(y + (size_t)t * H + i);
       v = make_float4(a.x + u.x, a.y + u.y, a.z + u.z, a.w + u.w);
     }
-    *reinterpret_cast<float4*>(rr + i) = v;
+    if (init != 2) *reinterpret_cast<float4*>(rr + i) = v;
     ss = __builtin_fmaf(v.x, v.x, ss);
     ss = __builtin_fmaf(v.y, v.y, ss);
     ss = __builtin_fmaf(v.z, v.z, ss);

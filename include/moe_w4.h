@@ -227,7 +227,10 @@ int moe_residual_rmsnorm(const float* y, float* resid, uint16_t* x, int32_t T, i
  * On entry x [T, H] bf16 holds the tokens; on return resid [T, H] fp32 holds the final
  * residual stream and x its normalised bf16 copy -- the input of the next decode step, left on
  * the device. All layers must share `hidden`. workspace: moe_stack_workspace_bytes(...)
- * (0 if invalid). Enqueue only, graph-capturable like moe_layer_forward. */
+ * (0 if invalid). Enqueue only, graph-capturable like moe_layer_forward. For decode-sized
+ * batches the residual update and the normalisation run inside the layers' own kernels (three
+ * launches per layer instead of four); the results are the same bits as the composition of
+ * moe_layer_forward and moe_residual_rmsnorm. */
 size_t moe_stack_workspace_bytes(const moe_layer_desc_t* const* layers, int32_t n_layers,
                                  int32_t T_max, int32_t flags);
 int moe_stack_forward(const moe_layer_desc_t* const* layers, int32_t n_layers, float* resid,

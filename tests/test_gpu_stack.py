@@ -101,7 +101,7 @@ def _layerwise(layers_dev, layers_host, name, T, flags, stream):
 
 
 @pytest.mark.parametrize("name,T,nl", [("mid", 13, 3), ("mid", 300, 3), ("full", 1, 2),
-                                       ("full", 512, 2)])
+                                       ("full", 512, 2), ("odd", 16, 2), ("solo", 1, 3)])
 def test_stack_matches_layerwise_and_oracle(name, T, nl):
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
