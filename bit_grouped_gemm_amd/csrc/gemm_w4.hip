@@ -164,11 +164,13 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
   }
   const bool wave_active = tval[0];
 
-  // ---- chunk slots: kNB = 2 (one chunk in flight). Blocks of up to 4 row tiles use one
-  // 16 KiB array per chunk, larger blocks two (rows 0-127, 128-255). Separate arrays let the
-  // compiler see that reads of one slot never depend on copies into another.
-  static_assert(NARR == kNArr, "two chunk slots of up to two arrays");
-  constexpr int kNB = 2;
+  // ---- chunk slots. Blocks of up to 4 row tiles use one 16 KiB array per chunk, larger
+  // blocks two (rows 0-127, 128-255). Separate arrays let the compiler see that reads of one
+  // slot never depend on copies into another. Blocks of one or two row tiles have little work
+  // per chunk, so a chunk's HBM round trip would dominate: they keep three chunks in flight
+  // (four slots); taller blocks keep one (two slots), which measured faster for them.
+  static_assert(NARR == kNArr, "up to four chunk slots of one array or two of two arrays");
+  constexpr int kNB = NT <= 2 ? 4 : 2;
   auto slot_lo = [&](int k) -> char* { return NT <= 4 ? lds.a[k] : lds.a[2 * k]; };
   auto slot_hi = [&](int k) -> char* { return NT <= 4 ? lds.a[k] : lds.a[2 * k + 1]; };
 
@@ -406,6 +408,53 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4_gate_up(GemmParams p, int ns
     default: MOE_GEMM_BLOCK(8); break;
   }
 #undef MOE_GEMM_BLOCK
+}
+
+// Gate/up for small batches (few rows per expert): block-map tiles are cut into pieces of at
+// most 64 rows (two row tiles), one per workgroup, and two workgroups share a CU, so that one
+// wave's dequantisation (most of the work when a chunk feeds only one or two row tiles) runs
+// while the other wave waits for memory or issues MFMAs. Work units are the first pieces of
+// all tiles (the shared expert's first), then the second, third and fourth pieces.
+constexpr int kGUSRows = 64;
+__global__ __launch_bounds__(256, 2) void k_gemm_w4_gate_up_small(GemmParams p, int nslices) {
+  constexpr int MODE = kGateUp;
+  __shared__ __attribute__((aligned(1024))) char lds0[kArrBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kArrBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[kArrBytes];
+  __shared__ __attribute__((aligned(1024))) char lds3[kArrBytes];
+  const LdsArrays lds{{lds0, lds1, lds2, lds3}};
+
+  const int nb = *p.num_blocks;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int hd = kXcds * (local / nslices) + xcd;  // work unit
+  const int slice = local % nslices;
+  constexpr int kPieces = kBlockM / kGUSRows;
+  const int rounds = (gridDim.x / kXcds) / nslices;  // units per quarter of the grid / kXcds
+  const int piece_units = kXcds * (rounds / kPieces);
+  const int hb = hd / piece_units;
+  const int jd = hd - hb * piece_units;
+  if (jd >= nb) return;
+  const int nsh = p.n_shared > 0 ? (p.TK / p.K + kBlockM - 1) / kBlockM : 0;
+  const int j = jd < nsh ? nb - nsh + jd : jd - nsh;  // block-map entry
+  const int4 blk = p.blocks[j];
+  const int e = blk.x;
+  const int m_len = blk.z - kGUSRows * hb;
+  if (m_len <= 0) return;
+  const int m0 = blk.y + kGUSRows * hb, row0 = blk.w + kGUSRows * hb;
+  const bool shared = e >= p.E;
+  const int kdim = shared ? p.kdim_shared : p.kdim_routed;
+  const int ncols = shared ? p.n_shared : p.n_routed;
+  const int slice0 = slice * 128;
+  if (slice0 >= ncols) return;  // uniform over the workgroup, before any barrier
+  const int ml = m_len < kGUSRows ? m_len : kGUSRows;
+  const bool su = kdim == 2048;
+  if (ml > 32) {
+    if (su) gemm_block<MODE, 2, 2, 16, kNArr>(p, lds, e, m0, ml, row0, shared, kdim, ncols, slice0);
+    else gemm_block<MODE, 2, 2, 0, kNArr>(p, lds, e, m0, ml, row0, shared, kdim, ncols, slice0);
+  } else {
+    if (su) gemm_block<MODE, 1, 2, 16, kNArr>(p, lds, e, m0, ml, row0, shared, kdim, ncols, slice0);
+    else gemm_block<MODE, 1, 2, 0, kNArr>(p, lds, e, m0, ml, row0, shared, kdim, ncols, slice0);
+  }
 }
 
 // ============================================================================ down
@@ -671,8 +720,14 @@ hipError_t launch_gemm_w4(int mode, const GemmParams& p, int max_blocks, hipStre
   // every (block, slice[, half]) of the remapping in the kernels appears once in the grid
   const int rounds = (max_blocks + kXcds - 1) / kXcds;
   if (mode == kGateUp) {
-    hipLaunchKernelGGL(k_gemm_w4_gate_up, dim3(kXcds * rounds * nslices), dim3(256), 0, s, p,
-                       nslices);
+    if ((size_t)p.TK <= (size_t)32 * p.E) {
+      // small batches (at most 32 rows per expert on average): 64-row pieces, two per CU
+      hipLaunchKernelGGL(k_gemm_w4_gate_up_small, dim3(kXcds * (kBlockM / kGUSRows) * rounds * nslices),
+                         dim3(256), 0, s, p, nslices);
+    } else {
+      hipLaunchKernelGGL(k_gemm_w4_gate_up, dim3(kXcds * rounds * nslices), dim3(256), 0, s, p,
+                         nslices);
+    }
   } else {
     // two halves: the first pieces of all tiles, then the second pieces
     const dim3 grid(kXcds * 2 * rounds * nslices);
