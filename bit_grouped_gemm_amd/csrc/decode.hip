@@ -33,13 +33,13 @@ namespace moe {
 
 namespace {
 constexpr int kCH = 4;  // 16-byte chunks (32 inputs) per lane of a gate/up row (H <= 2048)
-constexpr int kNB = 4;  // down rows requested per batch by one 16-lane group
+constexpr int kNB = 2;  // k_dec_c, batches of more than one token: entries requested per batch
 // k_dec_b runs one 16-wave workgroup per CU: a single wave per CU derives the top-k, so the
 // selection rounds of different workgroups do not share a SIMD's issue slots.
 constexpr int kDecBWaves = 16;
-// k_dec_c: output rows per 16-lane group (two for a single token, whose waves have one entry
-// each; one for larger batches, whose waves keep several entries in flight)
-__host__ __device__ constexpr int dec_c_rows(int tc) { return tc == 1 ? 2 : 1; }
+// k_dec_c: output rows per 16-lane group (two: one workgroup per eight rows, all resident at
+// once on the full-size layer)
+__host__ __device__ constexpr int dec_c_rows(int) { return 2; }
 }  // namespace
 
 struct DecodeArgs {
@@ -752,6 +752,9 @@ int device_cus() {
   return cached[dev];
 }
 constexpr size_t kDecLdsMax = 80 * 1024;  // two workgroups per CU (160 KiB of LDS)
+// k_dec_c's workgroups of up to 16 waves are alone on their CU (registers), so C may stage its
+// activations in up to this much LDS
+constexpr size_t kDecCLdsMax = 144 * 1024;
 }  // namespace
 
 size_t decode_route_bytes(const Dims& d) { return route_words(d.TK(), d.T) * 4; }
@@ -802,7 +805,7 @@ hipError_t launch_decode_layer(const Dims& d, const moe_layer_desc_t& desc, cons
   const int nwc = ent_max < 16 ? ent_max : 16;
   const int rgc = dec_c_rows(d.T <= 1 ? 1 : 2);
   const size_t lds_c_route = (route_words(d.TK(), d.T) + d.TK()) * 4 + (size_t)nwc * rgc * 64 * 4;
-  const bool a_lds = d.T > 1 && a_bytes + lds_c_route <= kDecLdsMax;
+  const bool a_lds = d.T > 1 && a_bytes + lds_c_route <= kDecCLdsMax;
   const size_t lds_c = (a_lds ? a_bytes : 0) + lds_c_route;
   const int nA = d.E + (d.Fs > 0 ? 1 + d.Fs : 0);
   const dim3 gA((nA + 3) / 4), gB(device_cus() * 4 / (kDecBWaves / 4)), gC(d.H / (4 * rgc)), blk(256);
