@@ -474,35 +474,69 @@ constexpr int kDBufBytes = kDRows * kDRowBytes;   // 32 KiB
 constexpr int kDCopies = kDBufBytes / 1024 / 4;   // 1 KiB LDS copies per wave and chunk
 }  // namespace
 
+// One K-chunk (8 MFMA steps of 16 inputs) for NT row tiles and the wave's two column tiles.
+// Software-pipelined so that the dequantisation runs between MFMAs of the same wave (on gfx950 a
+// wave's VALU work overlaps its MFMAs only when the two are interleaved): tile 0's MFMAs of step
+// s are interleaved with tile 1's dequantisation of step s, and tile 1's MFMAs with tile 0's
+// dequantisation and the A-fragment reads of step s + 1. Every accumulator takes the same MFMAs
+// in the same order as a step-by-step loop.
 template <int NT>
 __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, const uint4 (&q)[4],
                                                float s0, float b0, float s1, float b1,
                                                f32x16_t (&acc)[NT][2]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t w0 = (s < 4) ? ((const uint32_t*)&q[0])[s] : ((const uint32_t*)&q[1])[s - 4];
-    const uint32_t w1 = (s < 4) ? ((const uint32_t*)&q[2])[s] : ((const uint32_t*)&q[3])[s - 4];
-    uint32_t d0[4], d1[4];
-    dequant8(w0, s0, b0, d0);
-    dequant8(w1, s1, b1, d1);
-    const bf16x8_t bv0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<uint4*>(d0));
-    const bf16x8_t bv1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<uint4*>(d1));
-    const int off = (seg0 ^ s) << 4;
-    bf16x8_t av[NT];
+  auto deq = [&](int t, int s) -> bf16x8_t {
+    const uint4& v = q[2 * t + (s >> 2)];
+    const uint32_t w = (s & 3) == 0 ? v.x : (s & 3) == 1 ? v.y : (s & 3) == 2 ? v.z : v.w;
+    uint32_t d[4];
+    dequant8(w, t ? s1 : s0, t ? b1 : b0, d);
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<uint4*>(d));
+  };
+  auto read_a = [&](int s, bf16x8_t (&av)[NT]) {
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
-      av[mt] = *reinterpret_cast<const bf16x8_t*>(a_lane + mt * 32 * kDRowBytes + off);
+      av[mt] = *reinterpret_cast<const bf16x8_t*>(a_lane + mt * 32 * kDRowBytes + ((seg0 ^ s) << 4));
+  };
+  constexpr int kV = (22 + NT - 1) / NT;  // VALU instructions per MFMA (22 per dequantised word)
+  bf16x8_t av[NT];
+  read_a(0, av);
+  bf16x8_t bv0 = deq(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8_t bv1 = deq(1, s);
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
       acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv0, acc[mt][0], 0, 0, 0);
-      acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv1, acc[mt][1], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
     }
-    // keep each step's fragments within the step (bounds register pressure at two waves per
-    // SIMD)
     __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t avn[NT], bvn;
+    if (s < 7) {
+      bvn = deq(0, s + 1);
+      read_a(s + 1, avn);
+    }
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv1, acc[mt][1], 0, 0, 0);
+    if (s < 7) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s < 7) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) av[mt] = avn[mt];
+      bv0 = bvn;
+    }
   }
 }
-
 template <int MODE, int NT>
 __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char* buf1, int e,
                                            int m0, int m_len, int row0, bool shared, int kdim,
