@@ -466,11 +466,11 @@ constexpr int kDCopies = kDBufBytes / 1024 / 4;   // 1 KiB LDS copies per wave a
 }  // namespace
 
 // One K-chunk (8 MFMA steps of 16 inputs) for NT row tiles and the wave's two column tiles.
-// Software-pipelined so that the dequantisation runs between MFMAs of the same wave (on gfx950 a
-// wave's VALU work overlaps its MFMAs only when the two are interleaved): tile 0's MFMAs of step
-// s are interleaved with tile 1's dequantisation of step s, and tile 1's MFMAs with tile 0's
-// dequantisation and the A-fragment reads of step s + 1. Every accumulator takes the same MFMAs
-// in the same order as a step-by-step loop.
+// Software-pipelined so that the dequantisation can run between MFMAs of the same wave (on
+// gfx950 a wave's VALU work overlaps its MFMAs only when the two are interleaved): tile 0's
+// MFMAs of step s are grouped with tile 1's dequantisation of step s, and tile 1's MFMAs with
+// tile 0's dequantisation and the A-fragment reads of step s + 1; the compiler orders each group.
+// Every accumulator takes the same MFMAs in the same order as a step-by-step loop.
 template <int NT>
 __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, const uint4 (&q)[4],
                                                float s0, float b0, float s1, float b1,
@@ -487,7 +487,6 @@ __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, con
     for (int mt = 0; mt < NT; ++mt)
       av[mt] = *reinterpret_cast<const bf16x8_t*>(a_lane + mt * 32 * kDRowBytes + ((seg0 ^ s) << 4));
   };
-  constexpr int kV = (22 + NT - 1) / NT;  // VALU instructions per MFMA (22 per dequantised word)
   bf16x8_t av[NT];
   read_a(0, av);
   bf16x8_t bv0 = deq(0, 0);
@@ -498,11 +497,6 @@ __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, con
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
       acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv0, acc[mt][0], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
-    }
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t avn[NT], bvn;
     if (s < 7) {
@@ -512,14 +506,6 @@ __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, con
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
       acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mt], bv1, acc[mt][1], 0, 0, 0);
-    if (s < 7) {
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
     if (s < 7) {
 #pragma unroll
