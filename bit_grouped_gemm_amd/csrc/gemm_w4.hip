@@ -514,10 +514,15 @@ __device__ __forceinline__ void down_mma_chunk(const char* a_lane, int seg0, con
     }
   }
 }
-template <int MODE, int NT>
+// PR: rows of the piece a workgroup owns (128, or 32 for the small-batch kernel); the two
+// chunk buffers are PR rows of 256 B each.
+template <int MODE, int NT, int PR = kDRows>
 __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char* buf1, int e,
                                            int m0, int m_len, int row0, bool shared, int kdim,
                                            int ncols, int slice0) {
+  static_assert(NT * 32 <= PR, "the row tiles fit the piece");
+  constexpr int kBuf = PR * kDRowBytes;     // bytes per chunk buffer
+  constexpr int kCP = kBuf / 1024 / 4;      // 1 KiB LDS copies per wave and chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, half = lane >> 5;
@@ -539,7 +544,7 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
   const uint16_t* s1p = sb + r1 * gpr;
   const uint16_t* b1p = bb + r1 * gpr;
 
-  // ---- activation copies: wave w issues copies J = w*kDCopies + j, each 1 KiB = 4 rows of
+  // ---- activation copies: wave w issues copies J = w*kCP + j, each 1 KiB = 4 rows of
   // 256 B. Lane i fills LDS segment (i & 15) of row 4J + (i >> 4) with global segment
   // (i & 15) ^ (row & 15). Rows past the tile copy its first row (never stored) and segments
   // past kdim copy the row's first segment (their weights are zero), so every address is in
@@ -547,17 +552,17 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
   const uint16_t* abase = shared ? p.a_shared : p.a_routed;
   auto arow_of = [&](int r) -> int { return shared ? (m0 + r) : (row0 + r); };
   const int arow0 = arow_of(0);
-  uint32_t aoff[kDCopies];  // element offset of this lane's row for copy j
+  uint32_t aoff[kCP];  // element offset of this lane's row for copy j
   const int lseg = lane & 15;
 #pragma unroll
-  for (int j = 0; j < kDCopies; ++j) {
-    const int r = 4 * (wave * kDCopies + j) + (lane >> 4);
+  for (int j = 0; j < kCP; ++j) {
+    const int r = 4 * (wave * kCP + j) + (lane >> 4);
     aoff[j] = (uint32_t)(r < m_len ? arow_of(r) : arow0) * (uint32_t)kdim;
   }
   auto copy_a = [&](int c, char* buf) {
 #pragma unroll
-    for (int j = 0; j < kDCopies; ++j) {
-      const int J = wave * kDCopies + j;
+    for (int j = 0; j < kCP; ++j) {
+      const int J = wave * kCP + j;
       const int r = 4 * J + (lane >> 4);
       int k = c * kDKC + 8 * (lseg ^ (r & 15));
       if (k >= kdim) k = 0;
@@ -634,8 +639,8 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
     // different banks), then written back in 16-byte pieces: one store instruction covers
     // eight rows of 128 bytes. Column pairs are packed after a neighbour exchange: an even
     // lane n takes tile 0's columns (n, n + 1), an odd lane tile 1's columns (n - 1, n).
-    static_assert(kDRows * 128 <= kDBufBytes / 2, "a wave's staged tile fits half a buffer");
-    char* tile = (wave < 2 ? buf0 : buf1) + (wave & 1) * (kDBufBytes / 2);
+    static_assert(NT * 32 * 128 <= kBuf / 2, "a wave's staged tile fits half a buffer");
+    char* tile = (wave < 2 ? buf0 : buf1) + (wave & 1) * (kBuf / 2);
     const bool odd = (n & 1) != 0;
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
@@ -723,6 +728,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4_down(GemmParams p, int nslic
   }
 }
 
+// Down projection for small batches (the same condition as k_gemm_w4_gate_up_small): pieces of
+// at most 32 rows (one row tile) with 8 KiB chunk buffers, so that four workgroups share a CU
+// and one workgroup's dequantisation overlaps the others' loads. Work units are the first
+// pieces of all tiles, then the second, and so on; units without rows return at once.
+template <int MODE>
+__global__ __launch_bounds__(256, 4) void k_gemm_w4_down_small(GemmParams p, int nslices) {
+  constexpr int kRowsS = 32;
+  constexpr int kPieces = kBlockM / kRowsS;
+  __shared__ __attribute__((aligned(1024))) char lds0[kRowsS * kDRowBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kRowsS * kDRowBytes];
+  const int nb = *p.num_blocks;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int hd = kXcds * (local / nslices) + xcd;  // work unit
+  const int slice = local % nslices;
+  const int rounds = (gridDim.x / kXcds) / nslices;
+  const int piece_units = kXcds * (rounds / kPieces);
+  const int hb = hd / piece_units;
+  const int j = hd - hb * piece_units;
+  if (j >= nb) return;
+  const int4 blk = p.blocks[j];
+  const int e = blk.x;
+  const int m_len = blk.z - kRowsS * hb;
+  if (m_len <= 0) return;
+  const int m0 = blk.y + kRowsS * hb, row0 = blk.w + kRowsS * hb;
+  const bool shared = e >= p.E;
+  const int kdim = shared ? p.kdim_shared : p.kdim_routed;
+  const int ncols = shared ? p.n_shared : p.n_routed;
+  const int slice0 = slice * 256;
+  if (slice0 >= ncols) return;  // uniform over the workgroup, before any barrier
+  const int ml = m_len < kRowsS ? m_len : kRowsS;
+  down_block<MODE, 1, kRowsS>(p, lds0, lds1, e, m0, ml, row0, shared, kdim, ncols, slice0);
+}
+
 hipError_t launch_gemm_w4(int mode, const GemmParams& p, int max_blocks, hipStream_t s) {
   const int ncols = p.n_routed > p.n_shared ? p.n_routed : p.n_shared;
   const int slice = (mode == kGateUp) ? 128 : 256;
@@ -740,6 +778,15 @@ hipError_t launch_gemm_w4(int mode, const GemmParams& p, int max_blocks, hipStre
                          nslices);
     }
   } else {
+    if ((size_t)p.TK <= (size_t)32 * p.E) {
+      // small batches: 32-row pieces, four workgroups per CU
+      const dim3 grid(kXcds * (kBlockM / 32) * rounds * nslices);
+      if (mode == kDownStore)
+        hipLaunchKernelGGL(k_gemm_w4_down_small<kDownStore>, grid, dim3(256), 0, s, p, nslices);
+      else
+        hipLaunchKernelGGL(k_gemm_w4_down_small<kDownAtomic>, grid, dim3(256), 0, s, p, nslices);
+      return hipGetLastError();
+    }
     // two halves: the first pieces of all tiles, then the second pieces
     const dim3 grid(kXcds * 2 * rounds * nslices);
     if (mode == kDownStore)
