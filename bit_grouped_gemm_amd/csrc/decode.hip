@@ -32,7 +32,6 @@
 namespace moe {
 
 namespace {
-constexpr int kCH = 4;  // 16-byte chunks (32 inputs) per lane of a gate/up row (H <= 2048)
 constexpr int kNB = 2;  // k_dec_c, batches of more than one token: entries requested per batch
 // k_dec_b runs one 16-wave workgroup per CU: a single wave per CU derives the top-k, so the
 // selection rounds of different workgroups do not share a SIMD's issue slots.
@@ -558,6 +557,12 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
   float* part = reinterpret_cast<float*>(A_LDS ? (void*)(as + a_elems) : (void*)smem);  // [NW][kRG][64]
   const Route R = carve_route(part + 64 * kRG * NW, TK, T);
 
+  // inside the stack the residual values this wave adds the layer output to are requested
+  // first, so that the final update does not wait for them
+  float rold[kRG];
+#pragma unroll
+  for (int r = 0; r < kRG; ++r)
+    rold[r] = p.acc_out && sl < T && r % NW == wave % NW ? p.out[(size_t)sl * H + h0 + 4 * r] : 0.0f;
   const int nw = (int)route_words(TK, T);
   for (int i = tid; i < nw; i += (int)blockDim.x) R.nd[i] = p.b.route[i];
   __syncthreads();
@@ -731,8 +736,8 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
     if (sl < T) {
       float v = part[r * 64 + lane];
       for (int w = 1; w < NW; ++w) v += part[(w * kRG + r) * 64 + lane];
-      float* o = p.out + (size_t)sl * H + h0 + 4 * r;
-      *o = p.acc_out ? *o + v : v;  // inside the stack: the residual update r + y
+      // inside the stack: the residual update r + y
+      p.out[(size_t)sl * H + h0 + 4 * r] = p.acc_out ? rold[r] + v : v;
     }
   }
 }

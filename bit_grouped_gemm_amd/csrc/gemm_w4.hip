@@ -462,7 +462,6 @@ constexpr int kDKC = 128;                         // inputs per K-chunk
 constexpr int kDRowBytes = kDKC * 2;              // one activation row of a chunk in LDS
 constexpr int kDRows = kBlockM / 2;               // rows per workgroup (half a block)
 constexpr int kDBufBytes = kDRows * kDRowBytes;   // 32 KiB
-constexpr int kDCopies = kDBufBytes / 1024 / 4;   // 1 KiB LDS copies per wave and chunk
 }  // namespace
 
 // One K-chunk (8 MFMA steps of 16 inputs) for NT row tiles and the wave's two column tiles.
