@@ -61,11 +61,13 @@ def test_layer_matches_oracle(name, T, flags):
     check(name, T, flags, y, ref, ref_exact, ties, swapped)
 
 
-@pytest.mark.parametrize("name,flags", [("full", 0), ("full_skew", 0), ("full", ATOMIC)])
-def test_prefill_full_size_sampled(name, flags):
-    """T = 4096 at the full layer size (the timed prefill workload); the oracle checks 40
-    sampled tokens one by one, including the first and the last."""
-    T = 4096
+@pytest.mark.parametrize("name,flags,T", [("full", 0, 4096), ("full_skew", 0, 4096),
+                                          ("full", ATOMIC, 4096), ("full", 0, 512),
+                                          ("full_skew", 0, 512), ("full_skew", ATOMIC, 512)])
+def test_prefill_full_size_sampled(name, flags, T):
+    """T = 4096 at the full layer size (the timed prefill workload) and T = 512 (a prefill
+    chunk: the small-batch GEMM kernels, with blocks of hundreds of rows under skewed routing);
+    the oracle checks 40 sampled tokens one by one, including the first and the last."""
     log(f"[layer] start {name} T={T} flags={flags} (sampled)")
     layer, xh, x, y = run_layer(name, T, flags)
     host = host_layer(name)
