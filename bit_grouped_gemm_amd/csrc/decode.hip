@@ -20,7 +20,8 @@
 //     counting; a single token's experts are its ranks), and its waves stream the selected
 //     experts' gate/up rows (a 1 KiB row per wave, 16 bytes per lane), dequantise them in
 //     registers and store A = bf16(silu(G) * U); workgroup 0 also stores the per-expert route
-//     record for C;
+//     record for C. For a single token a wave requests its expert's rows as soon as the
+//     selection has chosen that rank, while the later ranks are still being selected;
 //   C (k_dec_c): down projection fused with the weighted combine of the bf16-rounded expert
 //     outputs. A workgroup owns four output rows (one per 16-lane group) and has one wave
 //     per entry (the selected experts, the shared expert last; at most 16 waves, which then
@@ -436,25 +437,34 @@ __global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
       tmask[e] = 0u;
     }
   if (tid < T && Fs > 0) R.sgs[tid] = 1.0f / (1.0f + __expf(-glog));
+  if (T == 1 && tid < K) {
+    // one token: its K experts are distinct, so the entries are the ranks themselves (entry k =
+    // the rank-k expert, one row, A row k); no grouping pass is needed. ent_e[k] = -1 until
+    // the top-k has chosen rank k.
+    R.ent_e[tid] = -1;
+    R.ent_m[tid] = 1;
+    R.ent_row0[tid] = tid;
+    R.ent_mask[tid] = 1u;
+    R.row_tok[tid] = 0;
+    if (tid == 0) *R.nd = K;
+  }
   __syncthreads();
   if (T == 1) {
-    // one token: its K experts are distinct, so the entries are the ranks themselves (entry k =
-    // the rank-k expert, one row, A row k); no grouping pass is needed
+    // Wave 0 publishes each rank's expert as soon as its round has chosen it; the other waves
+    // wait for the rank of their task only (below) and request its rows while the later
+    // rounds still run, so most of the weight traffic overlaps the selection.
     if (wave == 0) {
       float my_v, my_w;
       int my_i;
-      wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w);
-      if (lane < K) {
-        R.ent_e[lane] = my_i;
-        R.ent_m[lane] = 1;
-        R.ent_row0[lane] = lane;
-        R.ent_mask[lane] = 1u;
-        R.row_w[lane] = my_w;
-        R.row_tok[lane] = 0;
+      wave_topk_softmax<NJ>(lv, E, K, lane, my_v, my_i, my_w, [&](int r, int I) {
+        if (lane == 0) __hip_atomic_store(R.ent_e + r, I, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      });
+      if (lane < K) R.row_w[lane] = my_w;
+      if (blockIdx.x == 0) {  // the route record for the down projection (this wave's writes)
+        const int n = (int)route_words(TK, T);
+        for (int i = lane; i < n; i += 64) p.b.route[i] = R.nd[i];
       }
-      if (lane == 0) *R.nd = K;
     }
-    __syncthreads();
   } else {
     for (int t = wave; t < T; t += kDecBWaves) {
       if (t != wave) load_logits<NJ>(p.b.logits + (size_t)t * E, E, lane, lv);
@@ -470,16 +480,31 @@ __global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
     }
     __syncthreads();
     build_route(R, sel_idx, sel_w, cnt, tmask, off, T, E, K);
+    if (blockIdx.x == 0) {  // the route record for the down projection
+      const int n = (int)route_words(TK, T);
+      for (int i = tid; i < n; i += 64 * kDecBWaves) p.b.route[i] = R.nd[i];
+    }
   }
-  if (blockIdx.x == 0) {  // the route record for the down projection
-    const int n = (int)route_words(TK, T);
-    for (int i = tid; i < n; i += 64 * kDecBWaves) p.b.route[i] = R.nd[i];
-  }
-  const int D = *R.nd;
+  const int D = T == 1 ? K : *R.nd;
+  // expert of entry d: for one token, wait until wave 0 has published it (it always publishes
+  // all K ranks, so the wait ends); the value is read once per wave (readfirstlane)
+  auto expert_of = [&](int d) -> int {
+    if (T > 1) return R.ent_e[d];
+    int e;
+    while ((e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                R.ent_e + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))) < 0)
+      __builtin_amdgcn_s_sleep(1);
+    return e;
+  };
 
   // Tasks task = gw + NW*i, in batches of kPB; the next batch's rows are requested before the
-  // current batch is used. A batch requests no rows past the last task.
+  // current batch is used. A batch requests no rows past the last task. Task tk is row f of
+  // entry d: for one token d = tk % K, so a workgroup's waves spread over the ranks and the
+  // rows that wait for the last rounds of the selection are shared out over all CUs; for
+  // several tokens d = tk / F (an entry's rows on neighbouring waves).
   const int nB = D * F;
+  auto task_d = [&](int tk) { return T == 1 ? tk % K : tk / F; };
+  auto task_f = [&](int tk) { return T == 1 ? tk / K : tk % F; };
   constexpr int kPB = 2;
   const int step = kPB * NW;
   auto issue = [&](PairW (&w)[kPB], int t0) {
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
     for (int b = 0; b < kPB; ++b) {
       const int tk = t0 + b * NW;
       if (b == 0 || tk < nB)  // uniform over the wave; t0 < nB at every call
-        load_pair(w[b], p.gate, p.up, (size_t)R.ent_e[tk / F] * F + tk % F, H, lane);
+        load_pair(w[b], p.gate, p.up, (size_t)expert_of(task_d(tk)) * F + task_f(tk), H, lane);
     }
   };
   auto run = [&](const PairW (&w)[kPB], int t0) {
@@ -495,7 +520,7 @@ __global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
     for (int b = 0; b < kPB; ++b) {
       const int tk = t0 + b * NW;
       if (tk < nB) {  // uniform over the wave
-        const int d = tk / F, f = tk % F;
+        const int d = task_d(tk), f = task_f(tk);
         const int m = __builtin_amdgcn_readfirstlane(R.ent_m[d]);
         const int row0 = R.ent_row0[d];
         auto a_row = [&](int j) { return (size_t)(row0 + j) * F; };

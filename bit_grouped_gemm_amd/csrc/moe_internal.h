@@ -245,10 +245,15 @@ __device__ __forceinline__ float key_value(int k) {
 //      ballot; that lane drops its head.
 // Lane r < K ends with the rank-r expert my_i, its logit my_v and its renormalised weight
 // my_w = exp(my_v - M_0) / sum_r exp(M_r - M_0), the sum taken in rank order; lanes >= K get
-// my_w = 0.
-template <int NJ>
+// my_w = 0. on_rank(r, I) runs on the whole wave as soon as round r has chosen expert I
+// (uniform), so a caller can hand each rank on before the later rounds finish.
+struct NoRankHook {
+  __device__ void operator()(int, int) const {}
+};
+template <int NJ, typename OnRank = NoRankHook>
 __device__ __forceinline__ void wave_topk_softmax(const float (&v)[NJ], int E, int K, int lane,
-                                                  float& my_v, int& my_i, float& my_w) {
+                                                  float& my_v, int& my_i, float& my_w,
+                                                  OnRank on_rank = OnRank()) {
   // composite: order key (sign flipped to unsigned order) above the complemented index, so a
   // larger composite is earlier in the order
   uint64_t c[NJ];
@@ -279,6 +284,7 @@ __device__ __forceinline__ void wave_topk_softmax(const float (&v)[NJ], int E, i
     const int M = wave_max_i32(key[0]);
     const int L = (int)__builtin_ctzll(__ballot(key[0] == M));
     const int I = __builtin_amdgcn_readlane(idx[0], L);
+    on_rank(r, I);
     if (lane == L) {
 #pragma unroll
       for (int j = 0; j + 1 < NJ; ++j) {
