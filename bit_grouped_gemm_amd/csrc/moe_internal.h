@@ -11,6 +11,7 @@ namespace moe {
 
 constexpr int kBlockM = MOE_BLOCK_M;  // rows per grouped-GEMM tile (block-map granularity)
 constexpr int kChunkSlots = 1024;     // slots per permutation chunk (one histogram row each)
+constexpr int kPermuteOneMax = 8192;  // up to this many slots the permutation is one workgroup
 constexpr int kDecodeMaxT = 16;       // largest T served by the decode (GEMV) kernels
 constexpr int kGroup = 64;            // quantisation group along the input dimension
 

@@ -183,6 +183,106 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
   }
 }
 
+// Up to kPermuteOneMax slots in one workgroup of 16 waves, with the results of the three passes
+// above and no launches between them: wave w takes the w-th sixteenth of the slots (a multiple
+// of 64 slots, held in registers from the first pass to the last) and counts it per expert in
+// LDS; thread e then forms expert e's count, offset,
+// blocks and the running position of each sixteenth (the offset plus the counts of the lower
+// sixteenths); finally every wave scatters its sixteenth in slot order with the peer ranks of
+// k_scatter. Inside an expert the slots therefore stay ascending, as in the three-pass path.
+__global__ __launch_bounds__(1024) void k_permute_one(
+    const int32_t* __restrict__ idx, int TK, int E, int T, int K, int has_shared, int nbits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ blocks,
+    int32_t* __restrict__ num_blocks, int32_t* __restrict__ sorted_slots,
+    int32_t* __restrict__ slot_pos) {
+  extern __shared__ int cur[];  // [16][E]
+  __shared__ int wave_tot[16];
+  __shared__ int total_slots, total_blocks, bad;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < 16 * E; i += 1024) cur[i] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  const int per = (TK + 16 * 64 - 1) / (16 * 64) * 64;  // slots per wave
+  const int q0 = wave * per, q1 = min(TK, q0 + per);
+  int* my = cur + wave * E;
+  // this wave's ids, all requested at once and kept in registers for the scatter (step i holds
+  // slots q0 + 64i .. q0 + 64i + 63; -1 past the end), then counted per expert
+  constexpr int kSteps = kPermuteOneMax / (16 * 64);
+  int ev[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s = q0 + 64 * i + lane;
+    ev[i] = (64 * i < per && s < q1) ? idx[s] : -1;
+  }
+  int nbad = 0;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s = q0 + 64 * i + lane;
+    if (64 * i < per && s < q1) {
+      if (ev[i] >= 0 && ev[i] < E)
+        atomicAdd(&my[ev[i]], 1);
+      else
+        ++nbad;
+    }
+  }
+  if (nbad) atomicAdd(&bad, nbad);
+  __syncthreads();
+  const int ex = tid;
+  int cnt = 0;
+  if (ex < E)
+    for (int w = 0; w < 16; ++w) cnt += cur[w * E + ex];
+  const int off = block_exclusive_scan_1024(ex < E ? cnt : 0, wave_tot, &total_slots);
+  if (ex < E) {
+    counts[ex] = cnt;
+    offsets[ex] = off;
+    int run = off;
+    for (int w = 0; w < 16; ++w) {
+      const int c = cur[w * E + ex];
+      cur[w * E + ex] = run;
+      run += c;
+    }
+  }
+  const int nb = (ex < E) ? (cnt + kBlockM - 1) / kBlockM : 0;
+  const int boff = block_exclusive_scan_1024(nb, wave_tot, &total_blocks);
+  if (ex == 0) offsets[E] = total_slots;
+  for (int j = 0; j < nb; ++j) {
+    const int m0 = j * kBlockM;
+    blocks[boff + j] = make_int4(ex, m0, min(kBlockM, cnt - m0), off + m0);
+  }
+  const int nbs = has_shared ? (T + kBlockM - 1) / kBlockM : 0;
+  for (int j = tid; j < nbs; j += 1024) {
+    const int m0 = j * kBlockM;
+    blocks[total_blocks + j] = make_int4(E, m0, min(kBlockM, T - m0), T * K + m0);
+  }
+  __syncthreads();  // the running positions are complete
+  if (tid == 0) *num_blocks = bad ? -1 : total_blocks + nbs;
+  // scatter in slot order
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    if (64 * i >= per) break;  // uniform
+    const int s = q0 + 64 * i + lane;
+    const int e = ev[i];
+    const bool ok = s < q1 && e >= 0 && e < E;
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t lower = peers & ((1ull << lane) - 1ull);
+    int p = 0;
+    if (ok) p = my[e] + __popcll(lower);
+    // the wave's own LDS accesses complete in order: every lane's read of my[e] above comes
+    // before the lowest peer's update below
+    if (ok && lower == 0) my[e] += __popcll(peers);
+    if (ok) {
+      sorted_slots[p] = s;
+      slot_pos[s] = p;
+    }
+  }
+}
+
 // Decode routing in one workgroup (T <= 16 tokens, E <= 1024): wave t selects token t's top-k
 // (softmax-renormalised) and its shared gate, then the workgroup builds counts, offsets,
 // the block map (one block per active expert: an expert holds at most T < 128 rows) and the
@@ -269,6 +369,13 @@ hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_
   const int nchunks = (TK + kChunkSlots - 1) / kChunkSlots;
   int nbits = 0;
   while ((1 << nbits) < d.E) ++nbits;
+  if (TK <= kPermuteOneMax) {
+    hipLaunchKernelGGL(k_permute_one, dim3(1), dim3(1024), (size_t)16 * d.E * sizeof(int), s, idx,
+                       TK, d.E, d.T, d.K, shared ? 1 : 0, nbits, plan.counts, plan.offsets,
+                       reinterpret_cast<int4*>(plan.blocks), plan.num_blocks, plan.sorted_slots,
+                       plan.slot_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(256), 0, s, idx, TK, d.E, hist);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, nchunks, d.E, d.T, d.K,
                      shared ? 1 : 0, plan.counts, plan.offsets,

@@ -84,6 +84,9 @@ def _routing(T, E, K, rng, skew=False):
     (16, 2, 4, 64, False), (7, 3, 1000, 64, False), (32, 4, 300, 0, False), (256, 8, 1, 64, False),
     (256, 8, 8, 64, False), (256, 8, 4096, 64, False), (256, 8, 4096, 64, True),
     (1024, 32, 200, 64, False), (1024, 1, 1, 0, False), (64, 32, 130, 64, False),
+    # up to 8192 slots the permutation is one workgroup, above it three passes (histogram
+    # rows, scan, scatter): both sides of the limit
+    (256, 8, 1024, 64, True), (256, 8, 1025, 64, False), (128, 32, 1100, 0, False),
 ])
 def test_permute_matches_oracle(E, K, T, Fs, skew):
     import torch
