@@ -590,10 +590,9 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
     rold[r] = p.acc_out && sl < T && r % NW == wave % NW ? p.out[(size_t)sl * H + h0 + 4 * r] : 0.0f;
   const int nw = (int)route_words(TK, T);
   for (int i = tid; i < nw; i += (int)blockDim.x) R.nd[i] = p.b.route[i];
-  __syncthreads();
-  const int D = *R.nd;
-  const int nD = D + (Fs > 0 ? 1 : 0);  // the shared expert is the last entry
-  const int ni = wave < nD ? (nD - wave + NW - 1) / NW : 0;  // entries of this wave
+  // D entries (a single token's are its K ranks, known before the route record arrives), the
+  // shared expert last; ni of them on this wave
+  int D = TC == 1 ? p.K : 0, nD = 0, ni = 0;
   const uint16_t* abase = A_LDS ? as : p.b.a;
 
   // Entries i0 .. i0+kB-1 of this wave; none past the wave's list is requested. Lanes past a
@@ -731,12 +730,25 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
   };
 
   // The first batch is requested as soon as the route record is in LDS; the activations are
-  // staged (A_LDS) while those loads are in flight.
+  // staged (A_LDS) while those loads are in flight. For a single token the shared expert's
+  // entry (the first of wave K when there are more than K waves) depends on no routing: that
+  // wave requests it before the route record has arrived and has it multiplied while the other
+  // waves still wait for their rows.
   float acc[kRG];
 #pragma unroll
   for (int r = 0; r < kRG; ++r) acc[r] = 0.0f;
   Batch b0, b1;
-  if (ni > 0) load_down(0, b0);
+  const bool early = TC == 1 && Fs > 0 && wave == D;
+  if (early) {
+    nD = D + 1;
+    ni = 1;
+    load_down(0, b0);
+  }
+  __syncthreads();  // the route record is in LDS
+  if (TC != 1) D = *R.nd;
+  nD = D + (Fs > 0 ? 1 : 0);
+  ni = wave < nD ? (nD - wave + NW - 1) / NW : 0;
+  if (ni > 0 && !early) load_down(0, b0);
   __builtin_amdgcn_sched_barrier(0);
   if (A_LDS) {
     stage_pieces<8>(reinterpret_cast<uint4*>(as), reinterpret_cast<const uint4*>(p.b.a),
