@@ -64,13 +64,15 @@ class LayerShape:
 # layer (input dimensions that end in half a K-chunk, a non-power-of-two expert count), a
 # layer wider than 2048 (its decode calls take the general GEMV kernels), and the full-size
 # Qwen3.6-35B-A3B MoE layer (uniform and skewed routing). "solo" has one expert per token and
-# no shared expert (the smallest entry list of the decode kernels).
+# no shared expert (the smallest entry list of the decode kernels); "many" sits at the largest
+# expert count and top-k the library accepts (1024 experts, top-32) with one-group down rows.
 SHAPES = {
     "tiny": LayerShape(256, 16, 2, 128, 128),
     "mid": LayerShape(512, 32, 4, 256, 192),
     "odd": LayerShape(320, 7, 3, 192, 64),
     "wide": LayerShape(2560, 16, 2, 128, 128),
     "solo": LayerShape(256, 8, 1, 128, 0),
+    "many": LayerShape(256, 1024, 32, 64, 64),
     "full": LayerShape(2048, 256, 8, 512, 512),
     "full_skew": LayerShape(2048, 256, 8, 512, 512, skewed=True),
 }

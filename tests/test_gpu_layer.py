@@ -26,6 +26,7 @@ CASES = [
     ("full", 1, 0), ("full", 8, 0), ("full", 16, 0), ("full", 8, FORCE),
     ("wide", 1, 0), ("wide", 4, 0), ("wide", 40, 0),
     ("solo", 1, 0), ("solo", 5, 0), ("solo", 40, 0),
+    ("many", 1, 0), ("many", 16, 0), ("many", 16, FORCE), ("many", 40, 0), ("many", 40, ATOMIC),
 ]
 
 
