@@ -20,7 +20,8 @@ FORCE = 2
 
 @pytest.mark.parametrize("name,T,flags", [("full", 1, 0), ("full", 8, 0), ("mid", 13, 0),
                                           ("mid", 300, 0), ("odd", 130, 0), ("odd", 16, FORCE),
-                                          ("full", 16, 0), ("wide", 4, 0)])
+                                          ("full", 16, 0), ("wide", 4, 0), ("many", 1, 0),
+                                          ("many", 40, 0)])
 def test_phases_reproduce_forward(name, T, flags):
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
@@ -101,7 +102,8 @@ def _layerwise(layers_dev, layers_host, name, T, flags, stream):
 
 
 @pytest.mark.parametrize("name,T,nl", [("mid", 13, 3), ("mid", 300, 3), ("full", 1, 2),
-                                       ("full", 512, 2), ("odd", 16, 2), ("solo", 1, 3)])
+                                       ("full", 512, 2), ("odd", 16, 2), ("solo", 1, 3),
+                                       ("many", 1, 2), ("many", 16, 2)])
 def test_stack_matches_layerwise_and_oracle(name, T, nl):
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
