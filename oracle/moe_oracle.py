@@ -27,10 +27,12 @@ Readings where the pages are silent (each also listed with its reason in the des
 
 Rounding profiles:
   * "exact": no intermediate rounding at all (the mathematical definition).
-  * "bf16": rounds (nearest, ties to even) exactly where [P1 "The Model ..."] says the
-    method's tensor operations take bf16: the reconstructed weights, the SwiGLU output that
-    feeds the down projection, and each expert's output (routed and shared), which feeds the
-    weighted combine. Everything else stays fp64.
+  * "bf16": rounds (nearest, ties to even) at exactly two places, the inputs of the two
+    tensor operations of an expert: the reconstructed weights ([P1 "The Model ..."]: the
+    4-bit weights are rebuilt into bf16 for the tensor operations, with fp32 accumulation)
+    and the SwiGLU output A that the down projection multiplies. The section says nothing of
+    the expert outputs, and the weighted combine is a scalar-weighted sum, not a tensor
+    operation, so the expert outputs, the combine and everything else stay fp64.
 
 Every function here is pinned by tests/test_oracle*.py against closed forms, brute force
 or invariants; no function is "parity unpinned".
@@ -152,14 +154,12 @@ def silu(z) -> np.ndarray:
 def expert_ffn(x, wg, wu, wd, profile: str = "exact") -> np.ndarray:
     """FFN(x) = Wd . (silu(Wg . x) * (Wu . x)) for rows x [n, H] (fp64 values).
 
-    In the "bf16" profile the SwiGLU output, which feeds the down projection's tensor
-    operation, and the expert's output, which feeds the weighted combine, are rounded to
-    bf16."""
+    In the "bf16" profile the SwiGLU output, the input of the down projection's tensor
+    operation, is rounded to bf16; the expert's output is not rounded."""
     a = silu(x @ wg.T) * (x @ wu.T)
     if profile == "bf16":
         a = round_to_bf16(a)
-    y = a @ wd.T
-    return round_to_bf16(y) if profile == "bf16" else y
+    return a @ wd.T
 
 
 def _mat(proj, e, profile):
