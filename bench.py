@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer throughput on one MI355X (tokens/s, and the fraction of the roofline).
 
-    python bench.py [--gpus 1] [--steps 640] [--warmup 64] [--only SECTION]
+    python bench.py [--gpus 1] [--steps 640] [--warmup 80] [--only SECTION]
 
 Workload (seeded synthetic data): the MoE layer of Qwen3.6-35B-A3B -- hidden 2048, 256 experts,
 top-8, expert FFN 512, one shared expert with FFN 512, 4-bit group-64 affine weights. A step is
@@ -16,8 +16,15 @@ one layer) and a pool of tokens, so every call streams its weights from HBM. Tim
 HIP-graph replays bracketed by device synchronisation and HIP events on the stream the kernels
 are launched on.
 
---only decode_t1 | decode_t8 | prefill_uniform | prefill_skewed | stack | copy runs one section (for profiler runs;
-"copy" is a plain 256 MiB device copy used to calibrate the memory counters) and prints no JSON.
+The headline times exactly --steps layer calls after --warmup untimed ones; latency
+percentiles (p10 / median / p90 per call) come from separate series of graph replays. The
+same run measures the ceilings the chip reaches in practice (a 1 GiB copy, a 1 GiB read, the
+library's MFMA-loop kernel) and reports every roofline fraction against both the datasheet
+peak and that measured ceiling. The CPU baseline is the fp64 oracle on bounded samples.
+
+--only decode_t1 | decode_t8 | prefill_uniform | prefill_skewed | stack | copy | peaks runs one
+section (for profiler runs; "copy" is a plain 256 MiB device copy and a 256 MiB read used to
+calibrate the memory counters) and prints no JSON.
 """
 from __future__ import annotations
 
@@ -44,11 +51,12 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=640, help="timed decode layer calls (T=1)")
-    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--warmup", type=int, default=80, help="untimed decode layer calls first")
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle CPU-baseline budget of the decode leg")
     ap.add_argument("--only", choices=["decode_t1", "decode_t8", "prefill_uniform",
-                                       "prefill_skewed", "stack", "copy"])
+                                       "prefill_skewed", "stack", "copy", "peaks"])
     ap.add_argument("--skip-cpu", action="store_true")
     return ap.parse_args()
 
@@ -110,31 +118,126 @@ class Pool:
         return self.tok[o:o + T]
 
 
-def graph_time(calls, reps: int, warm_reps: int) -> float:
-    """Capture `calls` (zero-argument launchers) into one HIP graph, replay it `warm_reps` times
-    untimed and `reps` times timed; return ms per call."""
+GRAPH_MAX_CALLS = 640
+
+
+def _capture(calls):
+    """Capture zero-argument launchers into HIP graphs of at most GRAPH_MAX_CALLS calls each
+    (after one eager pass that loads code objects and checks for errors)."""
     import torch
-    for c in calls:             # eager pass: loads code objects, checks for errors
+    for c in calls:
         c()
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for c in calls:
-            c()
-    for _ in range(warm_reps):
+    graphs = []
+    for i in range(0, len(calls), GRAPH_MAX_CALLS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in calls[i:i + GRAPH_MAX_CALLS]:
+                c()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_exact(timed, warm) -> float:
+    """Replay the `warm` calls untimed, then exactly the `timed` calls between two HIP events on
+    the stream the replays run on (the current stream); returns ms per timed call."""
+    import torch
+    gw = _capture(warm) if warm else []
+    gt = _capture(timed)
+    for g in gw:
         g.replay()
     torch.cuda.synchronize()
-    # replays run on the current stream; the events are recorded on that same stream
     cur = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(cur)
-    for _ in range(reps):
+    for g in gt:
         g.replay()
     e1.record(cur)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * len(calls))
+    return e0.elapsed_time(e1) / len(timed)
+
+
+def graph_time(calls, reps: int, warm_reps: int) -> float:
+    """One graph of `calls`, replayed `warm_reps` times untimed and `reps` times timed (one
+    event pair around all of them); returns ms per call."""
+    return replay_stats(calls, reps, warm_reps)["mean"]
+
+
+def replay_stats(calls, reps: int, warm_reps: int = 1) -> dict:
+    """One graph of `calls` replayed `reps` times, each replay between its own pair of events on
+    the replay stream: ms per call as the mean over all replays and the 10th, 50th and 90th
+    percentile over the replays."""
+    import numpy as np
+    import torch
+    (g,) = _capture(calls) if len(calls) <= GRAPH_MAX_CALLS else (None,)
+    assert g is not None, "replay_stats takes at most GRAPH_MAX_CALLS calls"
+    for _ in range(warm_reps):
+        g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(cur)
+    for r in range(reps):
+        g.replay()
+        ev[r + 1].record(cur)
+    torch.cuda.synchronize()
+    per = np.array([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]) / len(calls)
+    return {"mean": float(ev[0].elapsed_time(ev[reps]) / (reps * len(calls))),
+            "p10": float(np.percentile(per, 10)), "median": float(np.median(per)),
+            "p90": float(np.percentile(per, 90)), "replays": reps, "calls_per_replay": len(calls)}
+
+
+def pct_us(st: dict) -> dict:
+    """Latency percentiles in microseconds per call (over graph replays)."""
+    return {"p10": st["p10"] * 1e3, "median": st["median"] * 1e3, "p90": st["p90"] * 1e3,
+            "over": f"{st['replays']} graph replays of {st['calls_per_replay']} calls"}
+
+
+# ------------------------------------------------------------------------------ measured peaks
+def measured_peaks() -> dict:
+    """The ceilings this chip reaches in practice, beside the datasheet figures: a 1 GiB
+    device-to-device copy (bytes read + written per second), a 1 GiB read-only reduction, and
+    the MFMA-loop kernel of the library (independent bf16 MFMAs on every SIMD)."""
+    import torch
+    from bit_grouped_gemm_amd import moe_w4 as M
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    cur = torch.cuda.current_stream()
+
+    def best(fn, reps=5):
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            fn()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    b.copy_(a)
+    copy_ms = best(lambda: b.copy_(a))
+    sink = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    reads = {}
+    for wg in (1024, 2048):
+        M.moe_bench_stream_read(a, wg, sink)
+        reads[wg] = best(lambda: M.moe_bench_stream_read(a, wg, sink))
+    read_ms = min(reads.values())
+    flops = M.moe_bench_mfma_loop(1024, 200, sink)  # warm-up launch
+    flops = M.moe_bench_mfma_loop(1024, 20000, sink)
+    mfma_ms = best(lambda: M.moe_bench_mfma_loop(1024, 20000, sink), reps=3)
+    del a, b, sink
+    return {"copy_gbs": 2 * n / (copy_ms * 1e-3) / 1e9, "read_gbs": n / (read_ms * 1e-3) / 1e9,
+            "mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "how": "1 GiB device copy (read + write bytes); 1 GiB streaming read with 16-byte "
+                   "loads (library kernel, 1024 or 2048 workgroups); MFMA-loop kernel: 1024 "
+                   "workgroups x 4 waves x 20000 x 8 independent v_mfma_f32_32x32x16_bf16; "
+                   "best of 5 / 5 / 3 runs"}
 
 
 # ------------------------------------------------------------------------ algorithmic work
@@ -165,16 +268,21 @@ def gateup_flops(s, T):
     return 2.0 * s.H * 2 * s.F * T * s.K + 2.0 * s.H * 2 * s.Fs * T
 
 
+def down_flops(s, T):
+    return 2.0 * s.F * s.H * T * s.K + 2.0 * s.Fs * s.H * T
+
+
 # ----------------------------------------------------------------------------- sections
 def decode_section(pool: Pool, T: int, steps: int, warmup: int):
-    """Layer time at T tokens (all launches), then the dominant launch alone: phase 1 (top-k +
-    gate/up of the selected experts) replayed on workspaces prepared by a full call."""
+    """Exactly `steps` layer calls at T tokens (all launches; layers and tokens rotate), after
+    `warmup` untimed calls; latency percentiles over replays of 40 calls (each layer once);
+    then the dominant launch alone: phase 1 (top-k + gate/up of the selected experts) replayed
+    on workspaces prepared by a full call."""
     import numpy as np
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
     s = pool.shape
     L = pool.layers
-    n = 2 * len(L)                      # calls per graph: each layer twice, new tokens each time
     out = torch.empty((T, s.H), dtype=torch.float32, device="cuda")
     ws = M.alloc_workspace(L[0], T)
 
@@ -182,13 +290,13 @@ def decode_section(pool: Pool, T: int, steps: int, warmup: int):
         x = pool.token_slice(i, T)
         return lambda: M.moe_layer_forward(L[i % len(L)], x, out, ws)
 
-    reps, warm = max(1, math.ceil(steps / n)), max(1, math.ceil(warmup / n))
-    ms = graph_time([call(i) for i in range(n)], reps, warm)
+    ms = time_exact([call(i) for i in range(steps)], [call(i) for i in range(warmup)])
+    pct = replay_stats([call(i) for i in range(len(L))], 24)
 
     # the dominant kernel, live: per-call workspaces hold the state phase 1 starts from
     states = []
-    for i in range(n):
-        layer, x = L[i % len(L)], pool.token_slice(i, T)
+    for i in range(len(L)):
+        layer, x = L[i], pool.token_slice(i, T)
         wsi = M.alloc_workspace(layer, T)
         M.moe_layer_forward(layer, x, out, wsi)
         idx = torch.empty(T * s.K, dtype=torch.int32, device="cuda")
@@ -200,30 +308,45 @@ def decode_section(pool: Pool, T: int, steps: int, warmup: int):
     distinct = [int((st[3] > 0).sum().item()) for st in states]
     kb = float(np.mean([d * gateup_bytes(s, s.F) for d in distinct]))
     kb += T * (s.E + 1) * 4 + T * s.H * 2 + T * s.K * s.F * 2    # logits, x in; A out
-    kms = graph_time([(lambda st=st: M.moe_layer_forward_phase(st[0], st[1], out, st[2], 1))
-                      for st in states], max(2, reps), 1)
+    phases = {}
+    for ph, name in enumerate(("k_dec_a", "k_dec_b", "k_dec_c")):
+        phases[name] = replay_stats([(lambda st=st, ph=ph: M.moe_layer_forward_phase(
+            st[0], st[1], out, st[2], ph)) for st in states], 8)["mean"] * 1e3
     d_mean = float(np.mean(distinct))
-    return {"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "steps": reps * n,
-            "warmup": warm * n, "distinct_experts": d_mean,
-            "layer_bytes": decode_layer_bytes(s, T, d_mean),
+    return {"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "steps": steps,
+            "warmup": warmup, "distinct_experts": d_mean, "latency_us": pct_us(pct),
+            "layer_bytes": decode_layer_bytes(s, T, d_mean), "phases_us": phases,
             "kernel": {"name": "k_dec_b (top-k + gate/up of the selected experts)",
-                       "us": kms * 1e3, "bytes": kb}}
+                       "us": phases["k_dec_b"], "bytes": kb}}
+
+
+def padding_frac(counts, rows=32):
+    """Share of the MFMA rows that are padding: experts' rows rounded up to whole row tiles."""
+    import numpy as np
+    c = np.asarray(counts, dtype=np.int64)
+    padded = ((c + rows - 1) // rows * rows).sum()
+    return float(padded - c.sum()) / float(padded) if padded else 0.0
 
 
 def prefill_section(pool: Pool, steps: int, skewed: bool):
+    """Exactly `steps` layer calls at T = 4096 (layers rotate, two token batches alternate);
+    latency percentiles over replays of 8 calls; the time of each launch of the layer replayed
+    on its own on prepared workspaces."""
+    import numpy as np
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
     s = pool.shape
     L = pool.skew_layers if skewed else pool.layers
     T = T_PREFILL
-    n = min(steps, len(L))
     ws = M.alloc_workspace(L[0], T)
     out = torch.empty((T, s.H), dtype=torch.float32, device="cuda")
-    calls = [(lambda i=i: M.moe_layer_forward(L[i % len(L)], pool.prefill[i % 2], out, ws))
-             for i in range(n)]
-    reps = max(1, math.ceil(steps / n))
-    ms = graph_time(calls, reps, 1)
-    # the dominant kernel (phase 3: gate/up GEMM), on workspaces prepared by a full call
+
+    def call(i):
+        return lambda: M.moe_layer_forward(L[i % len(L)], pool.prefill[i % 2], out, ws)
+
+    ms = time_exact([call(i) for i in range(steps)], [call(i) for i in range(2)])
+    pct = replay_stats([call(i) for i in range(8)], 8)
+    # each launch on its own, on workspaces prepared by a full call
     nk = min(8, len(L))
     states = []
     for i in range(nk):
@@ -231,11 +354,28 @@ def prefill_section(pool: Pool, steps: int, skewed: bool):
         M.moe_layer_forward(L[i], pool.prefill[i % 2], out, wsi)
         states.append((L[i], pool.prefill[i % 2], wsi))
     torch.cuda.synchronize()
-    kms = graph_time([(lambda st=st: M.moe_layer_forward_phase(st[0], st[1], out, st[2], 3))
-                      for st in states], 3, 1)
-    return {"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "steps": reps * n,
-            "kernel": {"name": "k_gemm_w4<gate_up> (grouped GEMM, SwiGLU epilogue)",
-                       "us": kms * 1e3, "flops": gateup_flops(s, T)}}
+    names = ("router", "top-k", "permutation", "gate/up GEMM", "down GEMM", "combine")
+    assert M.moe_layer_num_phases(L[0], T) == len(names)
+    phases = {}
+    for ph, name in enumerate(names):
+        phases[name] = replay_stats([(lambda st=st, ph=ph: M.moe_layer_forward_phase(
+            st[0], st[1], out, st[2], ph)) for st in states], 6)["mean"] * 1e3
+    # routing of the timed batches: padding of the 32-row MFMA tiles
+    pads = []
+    for i in range(2):
+        cnt = torch.empty(s.E, dtype=torch.int32, device="cuda")
+        M.moe_route(L[i], pool.prefill[i], torch.empty(T * s.K, dtype=torch.int32, device="cuda"),
+                    torch.empty(T * s.K, device="cuda"), torch.empty(T, device="cuda"), cnt,
+                    M.alloc_workspace(L[i], T))
+        c = cnt.cpu().numpy()
+        pads.append(padding_frac(np.concatenate([c, [T]])))
+    return {"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "steps": steps,
+            "latency_us": pct_us(pct), "phases_us": phases,
+            "mfma_row_padding_frac": float(np.mean(pads)),
+            "kernel": {"name": "k_gemm_w4_gate_up (grouped GEMM, SwiGLU epilogue)",
+                       "us": phases["gate/up GEMM"], "flops": gateup_flops(s, T)},
+            "down_kernel": {"name": "k_gemm_w4_down (grouped GEMM, fp32 expert outputs)",
+                            "us": phases["down GEMM"], "flops": down_flops(s, T)}}
 
 
 def stack_section(pool: Pool):
@@ -255,18 +395,21 @@ def stack_section(pool: Pool):
     ws1 = stack.alloc_workspace(1)
     x1 = pool.token_slice(3, 1).clone()
     r1 = torch.empty((1, s.H), dtype=torch.float32, device="cuda")
-    ms_step = graph_time([lambda: stack.forward(r1, x1, ws1)], DECODE_STEPS_STACK, 8)
+    st = replay_stats([lambda: stack.forward(r1, x1, ws1)], DECODE_STEPS_STACK, 8)
+    ms_step = st["mean"]
     assert torch.isfinite(r1).all().item()
     return {"layers": len(pool.layers), "prefill_tokens": T_PREFILL, "chunk": CHUNK,
             "prefill_ms": prefill_ms, "prefill_tokens_per_s": T_PREFILL / (prefill_ms * 1e-3),
             "decode_steps": DECODE_STEPS_STACK, "decode_ms_per_token": ms_step,
             "decode_tokens_per_s": 1.0 / (ms_step * 1e-3),
+            "decode_latency_us": pct_us(st),
             "decode_hbm_frac": len(pool.layers) * decode_layer_bytes(s, 1, s.K) / (ms_step * 1e-3)
             / 1e9 / HBM_PEAK_GBS}
 
 
 def copy_section():
-    """A plain 256 MiB device-to-device copy (calibrates FETCH_SIZE / WRITE_SIZE)."""
+    """Calibration kernels for FETCH_SIZE / WRITE_SIZE: a plain 256 MiB device-to-device copy
+    (reads and writes 256 MiB) and a 256 MiB fp32 sum (reads 256 MiB, writes 4 bytes)."""
     import torch
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -274,14 +417,14 @@ def copy_section():
     a.fill_(1)
     for _ in range(3):
         b.copy_(a)
+    af = a.view(torch.float32)
+    for _ in range(3):
+        af.sum()
     torch.cuda.synchronize()
-    log(f"copied {n} bytes 3 times")
+    log(f"copied {n} bytes 3 times, summed {n} bytes 3 times")
 
 
-def cpu_baseline(pool: Pool, budget_s: float):
-    """The fp64 oracle on the host for T = 1 decode tokens of the same workload (layer 0),
-    repeated until the time budget is used; tokens/s."""
-    from oracle import moe_oracle as O
+def _blas_info():
     try:
         from threadpoolctl import threadpool_info
         info = threadpool_info()
@@ -289,29 +432,88 @@ def cpu_baseline(pool: Pool, budget_s: float):
         blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
     except Exception:  # pragma: no cover
         threads, blas = 1, "unknown"
+    return threads, blas
+
+
+def cpu_baseline(pool: Pool, budget_s: float):
+    """The fp64 oracle on the host (as it stands) for the same workload, on bounded samples:
+      * decode T = 1: whole layer calls of layer 0 on successive tokens until the budget is used;
+      * prefill T = 4096: the routing of all 4096 tokens, the shared expert on all of them, and
+        16 of the 256 routed experts on their routed rows, the expert time scaled by 256/16;
+      * 40-layer stack: 40 x (8 chunks of 512 tokens timed as above, 24 experts sampled) for the
+        prefill, 40 x the T = 1 layer time for a decode step.
+    Returns tokens/s figures; everything but the decode leg is labelled "extrapolated"."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    threads, blas = _blas_info()
+    host, s = pool.host0, pool.shape
     n, t0 = 0, time.time()
     while n < 2 or time.time() - t0 < budget_s:
-        O.layer_forward(pool.host0, pool.tok_host[n:n + 1], pool.shape.K, "bf16")
+        O.layer_forward(host, pool.tok_host[n:n + 1], s.K, "bf16")
         n += 1
     dt = time.time() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode tokens (T=1) through layer 0 of the full-size layer, fp64 NumPy "
-                      f"oracle, bf16 profile, {dt:.1f}s; BLAS={blas}, "
-                      f"host cpus={len(os.sched_getaffinity(0))}"}
+    decode_s = dt / n
+
+    def layer_time(xh, n_sample):
+        """Oracle seconds for one layer on tokens xh: routing + shared expert + all routed
+        experts, the latter extrapolated from n_sample experts spread over the expert ids."""
+        t = time.time()
+        logits = O.router_logits(xh, host["router_w"], host["router_bias"])
+        idx, p = O.select_topk(logits, s.K)
+        sg = O.shared_gate(xh, host["shared_gate_w"])
+        x = O.bf16_to_f64(xh)
+        deq = lambda nm, e: O.dequant(host[nm][0][e], host[nm][1][e], host[nm][2][e], "bf16")  # noqa: E731
+        ysh = O.expert_ffn(x, deq("sh_gate", 0), deq("sh_up", 0), deq("sh_down", 0), "bf16")
+        out = sg[:, None] * ysh
+        t_fixed = time.time() - t
+        t = time.time()
+        for e in np.linspace(0, s.E - 1, n_sample).astype(int):
+            tt, kk = np.nonzero(idx == e)
+            y = O.expert_ffn(x[tt], deq("gate", e), deq("up", e), deq("down", e), "bf16")
+            np.add.at(out, tt, p[tt, kk][:, None] * y)
+        return t_fixed + (time.time() - t) * s.E / n_sample
+
+    xp = pool.prefill_host[0]
+    prefill_s = layer_time(xp, 16)
+    chunk_s = layer_time(xp[:CHUNK], 24)
+    stack_prefill_s = N_LAYERS * (T_PREFILL // CHUNK) * chunk_s
+    stack_decode_s = N_LAYERS * decode_s
+    return {"value": 1.0 / decode_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode T=1: {n} tokens through layer 0 of the full-size layer in {dt:.1f}s "
+                      f"(fp64 NumPy oracle, bf16 profile); BLAS={blas}, "
+                      f"host cpus={len(os.sched_getaffinity(0))}",
+            "prefill_t4096": {"value": T_PREFILL / prefill_s, "unit": "tokens/s",
+                              "kind": "oracle, extrapolated",
+                              "sample": "routing and shared expert of all 4096 tokens, 16 of 256 "
+                                        "routed experts on their rows, scaled by 256/16"},
+            "stack_40_layers": {"prefill_tokens_per_s": T_PREFILL / stack_prefill_s,
+                                "decode_tokens_per_s": 1.0 / stack_decode_s,
+                                "kind": "oracle, extrapolated",
+                                "sample": "one 512-token chunk of layer 0 (24 of 256 experts, "
+                                          "scaled) x 8 chunks x 40 layers; decode: the T=1 layer "
+                                          "time x 40 layers"}}
 
 
-def roofline_hbm(k):
+def roofline_hbm(k, peaks=None):
     ach = k["bytes"] / (k["us"] * 1e-6) / 1e9
-    return {"bound": "hbm", "kernel": k["name"], "achieved": ach, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": k["bytes"],
-            "avg_launch_us": k["us"]}
+    r = {"bound": "hbm", "kernel": k["name"], "achieved": ach, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": k["bytes"],
+         "avg_launch_us": k["us"]}
+    if peaks:
+        r["measured_peak"] = max(peaks["copy_gbs"], peaks["read_gbs"])
+        r["frac_of_measured_peak"] = ach / r["measured_peak"]
+    return r
 
 
-def roofline_mfma(k):
+def roofline_mfma(k, peaks=None):
     ach = k["flops"] / (k["us"] * 1e-6) / 1e12
-    return {"bound": "mfma", "kernel": k["name"], "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "flops_per_launch": k["flops"],
-            "avg_launch_us": k["us"]}
+    r = {"bound": "mfma", "kernel": k["name"], "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+         "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "flops_per_launch": k["flops"],
+         "avg_launch_us": k["us"]}
+    if peaks:
+        r["measured_peak"] = peaks["mfma_bf16_tflops"]
+        r["frac_of_measured_peak"] = ach / r["measured_peak"]
+    return r
 
 
 def main():
@@ -330,31 +532,38 @@ def main():
     if args.only == "copy":
         copy_section()
         return
+    if args.only == "peaks":
+        log(f"peaks: {measured_peaks()}")
+        return
 
     pool = Pool(N_LAYERS)
     s = pool.shape
     t_all = time.time()
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
     if args.only == "decode_t1":
-        r = decode_section(pool, 1, args.steps, args.warmup)
-        log(f"decode T=1: {r['ms_per_step'] * 1e3:.2f} us/layer; k_dec_b {r['kernel']['us']:.2f} us")
+        r = decode_section(pool, 1, steps, warmup)
+        log(f"decode T=1: {r['ms_per_step'] * 1e3:.2f} us/layer; phases {r['phases_us']}")
         return
     if args.only == "decode_t8":
-        r = decode_section(pool, 8, args.steps // 2, args.warmup)
-        log(f"decode T=8: {r['ms_per_step'] * 1e3:.2f} us/layer; k_dec_b {r['kernel']['us']:.2f} us")
+        r = decode_section(pool, 8, steps, warmup)
+        log(f"decode T=8: {r['ms_per_step'] * 1e3:.2f} us/layer; phases {r['phases_us']}")
         return
     if args.only in ("prefill_uniform", "prefill_skewed"):
         r = prefill_section(pool, args.prefill_steps, args.only == "prefill_skewed")
-        log(f"{args.only}: {r['ms_per_step'] * 1e3:.1f} us/layer; gate/up {r['kernel']['us']:.1f} us")
+        log(f"{args.only}: {r['ms_per_step'] * 1e3:.1f} us/layer; phases {r['phases_us']}")
         return
     if args.only == "stack":
         r = stack_section(pool)
         log(f"stack: {r}")
         return
 
-    d1 = decode_section(pool, 1, args.steps, args.warmup)
+    peaks = measured_peaks()
+    log(f"measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, read {peaks['read_gbs']:.0f} GB/s, "
+        f"MFMA loop {peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
+    d1 = decode_section(pool, 1, steps, warmup)
     log(f"decode T=1: {d1['ms_per_step'] * 1e3:.2f} us/layer, {d1['tokens_per_s']:.0f} tok/s; "
-        f"k_dec_b {d1['kernel']['us']:.2f} us for {d1['kernel']['bytes'] / 1e6:.2f} MB")
-    d8 = decode_section(pool, 8, args.steps // 2, args.warmup)
+        f"phases {d1['phases_us']}")
+    d8 = decode_section(pool, 8, max(1, steps // 2), warmup)
     log(f"decode T=8: {d8['ms_per_step'] * 1e3:.2f} us/layer, {d8['tokens_per_s']:.0f} tok/s")
     prefill = {}
     for skewed in (False, True):
@@ -362,22 +571,27 @@ def main():
         p = prefill_section(pool, args.prefill_steps, skewed)
         fl = layer_flops(s, T_PREFILL)
         tf = fl / (p["ms_per_step"] * 1e-3) / 1e12
-        rk = roofline_mfma(p["kernel"])
+        rk = roofline_mfma(p["kernel"], peaks)
         rk["traffic"] = measured_traffic(f"gate_up@prefill_{tag}")
         prefill[tag] = {"value": p["tokens_per_s"], "unit": "tokens/s",
                         "ms_per_step": p["ms_per_step"], "steps": p["steps"],
+                        "latency_us": p["latency_us"],
                         "layer_tflops": tf, "layer_mfma_frac": tf / BF16_PEAK_TFLOPS,
-                        "roofline": rk}
+                        "layer_frac_of_measured_mfma_peak": tf / peaks["mfma_bf16_tflops"],
+                        "mfma_row_padding_frac": p["mfma_row_padding_frac"],
+                        "phases_us": p["phases_us"],
+                        "roofline": rk, "down_roofline": roofline_mfma(p["down_kernel"], peaks)}
         log(f"prefill T=4096 {tag}: {p['ms_per_step'] * 1e3:.1f} us/layer "
-            f"({p['tokens_per_s'] / 1e6:.2f} M tok/s, {tf:.0f} TFLOP/s); gate/up GEMM "
-            f"{p['kernel']['us']:.1f} us = {rk['achieved']:.0f} TFLOP/s")
+            f"({p['tokens_per_s'] / 1e6:.2f} M tok/s, {tf:.0f} TFLOP/s); phases {p['phases_us']}")
     st = stack_section(pool)
     log(f"stack ({st['layers']} layers): prefill {st['prefill_tokens_per_s']:.0f} tok/s, "
         f"decode {st['decode_tokens_per_s']:.0f} tok/s ({st['decode_ms_per_token'] * 1e3:.0f} us/token)")
+    log(f"timed sections took {time.time() - t_all:.1f}s")
     cpu = None if args.skip_cpu else cpu_baseline(pool, args.cpu_seconds)
 
-    roof = roofline_hbm(d1["kernel"])
+    roof = roofline_hbm(d1["kernel"], peaks)
     roof["traffic"] = measured_traffic("k_dec_b@decode_t1")
+    lbytes = d1["layer_bytes"] / (d1["ms_per_step"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": d1["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -387,21 +601,28 @@ def main():
         "config": {"workload": "MoE layer, decode T=1 (batch 1): hidden 2048, 256 experts, top-8, "
                                "expert FFN 512, one shared expert FFN 512, 4-bit group-64 affine",
                    "layer_pool": N_LAYERS, "token_pool": int(pool.tok.shape[0])},
+        "timing": f"exactly {d1['steps']} timed layer calls after {d1['warmup']} untimed ones, "
+                  f"replayed from HIP graphs of at most {GRAPH_MAX_CALLS} calls between two HIP "
+                  "events on the replay stream; layers rotate over the 40-layer pool",
         "roofline": roof,
         "cpu_baseline": cpu,
+        "latency_us": d1["latency_us"],
+        "phases_us": d1["phases_us"],
         "layer_bytes_per_token": d1["layer_bytes"],
-        "layer_hbm_frac": d1["layer_bytes"] / (d1["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_hbm_frac": lbytes / HBM_PEAK_GBS,
+        "layer_frac_of_measured_hbm_peak": lbytes / max(peaks["copy_gbs"], peaks["read_gbs"]),
+        "measured_peaks": peaks,
         "decode_t8": {"value": d8["tokens_per_s"], "unit": "tokens/s",
                       "ms_per_step": d8["ms_per_step"], "steps": d8["steps"],
+                      "latency_us": d8["latency_us"], "phases_us": d8["phases_us"],
                       "distinct_experts": d8["distinct_experts"],
                       "layer_hbm_frac": d8["layer_bytes"] / (d8["ms_per_step"] * 1e-3) / 1e9
                       / HBM_PEAK_GBS,
-                      "roofline": roofline_hbm(d8["kernel"])},
+                      "roofline": roofline_hbm(d8["kernel"], peaks)},
         "prefill_t4096": prefill,
         "stack_40_layers": st,
         "source_hash": kernel_source_hash(),
     }
-    log(f"timed sections took {time.time() - t_all:.1f}s")
     print(json.dumps(line), flush=True)
 
 

@@ -92,7 +92,9 @@ Layout layout_of(const Dims& d, int flags) {
   L.a = o;       o = align_up(o + (TK * d.F + (size_t)d.T * d.Fs) * 2);
   L.end_no_y = o;
   L.y = o;
-  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) o = align_up(o + (TK + d.T) * d.H * 2);  // bf16
+  // fp32 expert outputs for the deterministic (store + gather) combine; the fused atomic
+  // combine needs none
+  if (!(flags & MOE_FLAG_ATOMIC_COMBINE)) o = align_up(o + (TK + d.T) * d.H * 4);
   L.total = o;
   return L;
 }
@@ -103,6 +105,11 @@ T* at(void* ws, size_t off) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_HIP_ERROR; }
+
+// Known bits only.
+bool flags_ok(int flags) {
+  return !(flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_FORCE_PREFILL));
+}
 
 bool use_decode(const Dims& d, int flags) {
   return d.T <= kDecodeMaxT && !(flags & MOE_FLAG_FORCE_PREFILL) && d.F <= 512 && d.Fs <= 512 &&
@@ -177,7 +184,8 @@ bool plan_ok(const moe_plan_t* p) {
 //                             2 down + combine
 //   decode, other shapes:     0 router, 1 top-k + permutation, 2 gate/up, 3 down + combine
 //   prefill:                  0 router, 1 top-k, 2 permutation, 3 gate/up GEMM,
-//                             4 down GEMM, 5 combine   (atomic: 4 zero fill, 5 down + combine)
+//                             4 down GEMM storing fp32 Y, 5 combine
+//                             (MOE_FLAG_ATOMIC_COMBINE: 4 zero fill, 5 down GEMM + combine)
 int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* x, float* out,
                    void* ws, const Layout& L, int flags, hipStream_t s, int phase,
                    int* nphases) {
@@ -229,7 +237,7 @@ int layer_sequence(const moe_layer_desc_t* desc, const Dims& d, const uint16_t* 
         return launch_gemm_w4(kDownAtomic, pd, mb, s);
       });
     } else {
-      uint16_t* y = at<uint16_t>(ws, L.y);
+      float* y = at<float>(ws, L.y);
       step([&] {
         const GemmParams pd = gemm_params(desc, d, MOE_GEMM_DOWN, a, &plan, nullptr, nullptr, y);
         return launch_gemm_w4(kDownStore, pd, mb, s);
@@ -262,7 +270,7 @@ const char* moe_status_str(int status) {
 const char* moe_version(void) { return "moe_w4 1.0 gfx950"; }
 
 size_t moe_workspace_bytes(const moe_layer_desc_t* desc, int32_t T_max, int32_t flags) {
-  if (check_desc(desc) != MOE_OK || T_max < 0) return 0;
+  if (check_desc(desc) != MOE_OK || T_max < 0 || !flags_ok(flags)) return 0;
   const Dims d = dims_of(desc, T_max);
   if (!sizes_ok(d)) return 0;
   return layout_of(d, flags).total;
@@ -344,7 +352,7 @@ int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void*
   const Layout L = layout_of(d, 0);
   if (!workspace) return MOE_INVALID_ARG;
   if (ws_bytes < L.total) return MOE_WORKSPACE_TOO_SMALL;
-  uint16_t* y = at<uint16_t>(workspace, L.y);
+  float* y = at<float>(workspace, L.y);
   const GemmParams p = gemm_params(desc, d, MOE_GEMM_DOWN, in, plan, nullptr, nullptr, y);
   if (launch_gemm_w4(kDownStore, p, mb, s) != hipSuccess) return MOE_HIP_ERROR;
   return hip_status(launch_combine(y, plan->slot_pos, topk_w,
@@ -352,8 +360,8 @@ int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void*
                                    static_cast<float*>(out), s));
 }
 
-int moe_combine(const moe_layer_desc_t* desc, const uint16_t* y_perm, const int32_t* slot_pos,
-                const float* topk_w, const uint16_t* shared_y, const float* shared_gate,
+int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* shared_y, const float* shared_gate,
                 int32_t T, float* out, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
@@ -387,7 +395,7 @@ int moe_layer_forward_phase(const moe_layer_desc_t* desc, const uint16_t* x, int
                             int32_t phase, void* stream) {
   int st = check_desc(desc);
   if (st != MOE_OK) return st;
-  if (T < 0 || (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_FORCE_PREFILL))) return MOE_INVALID_ARG;
+  if (T < 0 || !flags_ok(flags)) return MOE_INVALID_ARG;
   if (T == 0) return MOE_OK;
   const Dims d = dims_of(desc, T);
   if (!sizes_ok(d)) return MOE_UNSUPPORTED;
@@ -484,6 +492,33 @@ int moe_debug_dequant_w4(const moe_w4_t* w, int32_t n_rows, int32_t Kin, int32_t
   if (!out_f32 && !out_bf16) return MOE_INVALID_ARG;
   return hip_status(launch_debug_dequant(*w, n_rows, Kin, mat, row, out_f32, out_bf16,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_debug_workspace_layout(const moe_layer_desc_t* desc, int32_t T, int32_t flags,
+                               size_t* offsets, int32_t n) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0 || !flags_ok(flags) || !offsets || n < 0) return MOE_INVALID_ARG;
+  const Dims d = dims_of(desc, T);
+  if (!sizes_ok(d)) return MOE_UNSUPPORTED;
+  const Layout L = layout_of(d, flags);
+  const size_t v[14] = {L.logits, L.topk_idx, L.topk_w,  L.sgate, L.droute, L.counts, L.offsets,
+                        L.sorted, L.slotpos,  L.blocks, L.nblk,  L.a,      L.y,      L.total};
+  for (int i = 0; i < n && i < 14; ++i) offsets[i] = v[i];
+  return MOE_OK;
+}
+
+int moe_bench_mfma_loop(int32_t workgroups, int32_t iters, float* sink, double* flops,
+                        void* stream) {
+  if (workgroups <= 0 || iters <= 0 || !sink || !flops) return MOE_INVALID_ARG;
+  *flops = mfma_loop_flops(workgroups, iters);
+  return hip_status(launch_mfma_loop(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
+int moe_bench_stream_read(const void* p, size_t bytes, int32_t workgroups, uint32_t* sink,
+                          void* stream) {
+  if (!p || !aligned(p, 16) || bytes % 16 || workgroups <= 0 || !sink) return MOE_INVALID_ARG;
+  return hip_status(launch_stream_read(p, bytes, workgroups, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,7 +1,7 @@
 // Weighted combine of the grouped expert outputs, and the dequantisation test export.
 //
 // The combine forms y[t] = sum_k p[t,k] * Y[slot_pos[t*K+k]] + sigmoid_gate[t] * Y_shared[t]
-// from the bf16 expert outputs Y, in fp32
+// from the fp32 expert outputs Y, in fp32
 // ("Perplexity's Lily: A Breakthrough Local Inference Engine Tailored Exclusively for Apple
 // Silicon", section "The Model: Qwen3.6-35B-A3B in Focus": eight routed experts plus one shared
 // expert per token). Terms are added in rank order, then the shared term: deterministic.
@@ -9,47 +9,51 @@
 
 namespace moe {
 
-// acc[j] += w * (element j of the 8 packed bf16 values in v)
-__device__ __forceinline__ void add_bf16x8(float (&acc)[8], float w, const uint4& v) {
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] = __builtin_fmaf(w, bf16_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
-    acc[2 * i + 1] = __builtin_fmaf(w, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
-  }
+__device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
+  acc.x = __builtin_fmaf(w, v.x, acc.x);
+  acc.y = __builtin_fmaf(w, v.y, acc.y);
+  acc.z = __builtin_fmaf(w, v.z, acc.z);
+  acc.w = __builtin_fmaf(w, v.w, acc.w);
 }
 
-// One workgroup per token; a thread takes 8 consecutive columns, one 16-byte piece of each
-// bf16 expert-output row.
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_perm,
+// One workgroup per token; a thread takes 4 consecutive columns (one 16-byte piece of each
+// expert-output row), all K rows requested before the first is used.
+template <int KC>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_perm,
                                                  const int32_t* __restrict__ slot_pos,
                                                  const float* __restrict__ topk_w,
-                                                 const uint16_t* __restrict__ shared_y,
+                                                 const float* __restrict__ shared_y,
                                                  const float* __restrict__ sgate, int H, int K,
                                                  float* __restrict__ out) {
   const int t = blockIdx.x;
-  const int h8n = H >> 3;
-  for (int h8 = threadIdx.x; h8 < h8n; h8 += 256) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = 0; k < K; ++k) {
-      const int s = t * K + k;
-      const uint4 v = reinterpret_cast<const uint4*>(y_perm + (size_t)slot_pos[s] * H)[h8];
-      add_bf16x8(acc, topk_w[s], v);
+  const int h4n = H >> 2;
+  for (int h4 = threadIdx.x; h4 < h4n; h4 += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < K; k0 += KC) {
+      float4 v[KC];
+      float w[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int k = k0 + j < K ? k0 + j : K - 1;  // past K: re-read the last row, weight 0
+        const int s = t * K + k;
+        v[j] = reinterpret_cast<const float4*>(y_perm + (size_t)slot_pos[s] * H)[h4];
+        w[j] = k0 + j < K ? topk_w[s] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (k0 + j < K) fma4(acc, w[j], v[j]);
     }
     if (shared_y != nullptr)
-      add_bf16x8(acc, sgate[t], reinterpret_cast<const uint4*>(shared_y + (size_t)t * H)[h8]);
-    float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * h8;
-    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      fma4(acc, sgate[t], reinterpret_cast<const float4*>(shared_y + (size_t)t * H)[h4]);
+    reinterpret_cast<float4*>(out + (size_t)t * H)[h4] = acc;
   }
 }
 
-hipError_t launch_combine(const uint16_t* y_perm, const int32_t* slot_pos, const float* topk_w,
-                          const uint16_t* shared_y, const float* sgate, const Dims& d, float* out,
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                          const float* shared_y, const float* sgate, const Dims& d, float* out,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(d.T), dim3(256), 0, s, y_perm, slot_pos, topk_w, shared_y,
-                     sgate, d.H, d.K, out);
+  hipLaunchKernelGGL(k_combine<8>, dim3(d.T), dim3(256), 0, s, y_perm, slot_pos, topk_w,
+                     shared_y, sgate, d.H, d.K, out);
   return hipGetLastError();
 }
 

@@ -22,8 +22,8 @@
 //     registers and store A = bf16(silu(G) * U); workgroup 0 also stores the per-expert route
 //     record for C. For a single token a wave requests its expert's rows as soon as the
 //     selection has chosen that rank, while the later ranks are still being selected;
-//   C (k_dec_c): down projection fused with the weighted combine of the bf16-rounded expert
-//     outputs. A workgroup owns four output rows (one per 16-lane group) and has one wave
+//   C (k_dec_c): down projection fused with the weighted combine of the fp32 expert outputs
+//     (fp32 accumulation, never rounded). A workgroup owns four output rows (one per 16-lane group) and has one wave
 //     per entry (the selected experts, the shared expert last; at most 16 waves, which then
 //     take several entries each); the waves' partial sums are added in LDS in wave order,
 //     so the result is deterministic.
@@ -561,7 +561,7 @@ struct DownW {
 // h = 4*(kRG*blockIdx.x + r) + g, r < kRG: 16-lane group g of every wave takes kRG rows
 // (one workgroup per CU for the full-size layer, all resident at once). Wave w walks the entries
 // d = w, w + NW, ... (ascending expert id, the shared expert last); lane sl of a group
-// accumulates, for token sl, the routing-weighted bf16-rounded expert outputs of the wave's
+// accumulates, for token sl, the routing-weighted fp32 expert outputs of the wave's
 // entries. The waves' sums are then added in LDS in wave order, so the result is deterministic.
 // The launcher sizes NW to the number of entries (at most 16): for a single token every wave
 // has exactly one entry, and each lane's 32 activations of that entry are requested from
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
           }
           group_reduce<1, 16>(one, sl);
           const float wgt = sh ? R.sgs[0] : R.row_w[row0];
-          if (sl == 0) acc = __builtin_fmaf(wgt, round_bf16(one[0]), acc);  // bf16 expert output
+          if (sl == 0) acc = __builtin_fmaf(wgt, one[0], acc);
           continue;
         } else {
           const int m = __builtin_amdgcn_readfirstlane(sh ? T : R.ent_m[d]);
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
             }
             group_reduce<1, 16>(one, sl);
             if (sl < T && ((tmask >> sl) & 1u))
-              acc = __builtin_fmaf(R.row_w[row0], round_bf16(one[0]), acc);
+              acc = __builtin_fmaf(R.row_w[row0], one[0], acc);
             continue;
           }
           float dots[TC];
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
             wgt = sh ? R.sgs[sl] : R.row_w[row0 + j];
           }
           const float val = __shfl(dots[0], (lane & ~15) + (j * 16) / TC, 64);
-          if (mine) acc = __builtin_fmaf(wgt, round_bf16(val), acc);  // the expert output in bf16
+          if (mine) acc = __builtin_fmaf(wgt, val, acc);
         }
       }
     }

@@ -630,62 +630,36 @@ __device__ __forceinline__ void down_block(const GemmParams& p, char* buf0, char
   if (!wave_active) return;
 
   // ---- epilogue. D layout (32x32): register i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-  // column l%32 of the tile. The expert outputs are rounded to bf16.
-  if constexpr (MODE == kDownStore) {
-    // The wave's 32*NT x 64 tile is staged in LDS as bf16 (16 KiB per wave: waves 0 and 1 in
-    // buffer 0, waves 2 and 3 in buffer 1; 128-byte rows whose 16-byte segment g sits at
-    // g ^ ((row >> 2) & 7), so rows r and r + 4 written by the two halves of the wave fall in
-    // different banks), then written back in 16-byte pieces: one store instruction covers
-    // eight rows of 128 bytes. Column pairs are packed after a neighbour exchange: an even
-    // lane n takes tile 0's columns (n, n + 1), an odd lane tile 1's columns (n - 1, n).
-    static_assert(NT * 32 * 128 <= kBuf / 2, "a wave's staged tile fits half a buffer");
-    char* tile = (wave < 2 ? buf0 : buf1) + (wave & 1) * (kBuf / 2);
-    const bool odd = (n & 1) != 0;
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const float v0 = acc[mt][0][i], v1 = acc[mt][1][i];
-        const float other = __shfl_xor(odd ? v0 : v1, 1, 64);  // the pair's other half
-        const uint32_t w = odd ? pack_bf16x2(other, v1) : pack_bf16x2(v0, other);
-        const int c = odd ? 32 + n - 1 : n;  // first column of the pair
-        const int seg = (c >> 3) ^ ((r >> 2) & 7);
-        *reinterpret_cast<uint32_t*>(tile + r * 128 + seg * 16 + 2 * (c & 7)) = w;
-      }
-    }
-    // a wave's LDS accesses complete in order: the reads below see this wave's writes
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)row0 * p.out_ld + slice0 + wave * 64;
-    const int q = lane & 7;
-    const bool qval = q < 4 || tile1;
-#pragma unroll
-    for (int pass = 0; pass < NT * 4; ++pass) {
-      const int r = pass * 8 + (lane >> 3);
-      const int seg = q ^ ((r >> 2) & 7);
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + r * 128 + seg * 16);
-      if (r < m_len && qval) *reinterpret_cast<uint4*>(orow + (size_t)r * p.out_ld + 8 * q) = v;
-    }
-    return;
-  }
+  // column l%32 of the tile. The expert outputs stay fp32 (the fp32 accumulators themselves).
+  // Store: register i of the 64 lanes covers 32 consecutive columns of two rows, i.e. two
+  // full 128-byte lines of Y, so the stores go straight from the accumulators.
+  // Atomic: out[t] += weight * Y row, the weighted combine fused into the epilogue.
+  float* const outf = static_cast<float*>(p.out);
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
       if (r >= m_len) continue;
-      int tok;
-      float wgt;
-      if (shared) {
-        tok = m0 + r;
-        wgt = p.shared_gate[tok];
+      if constexpr (MODE == kDownStore) {
+        float* orow = outf + (size_t)(row0 + r) * p.out_ld;
+        orow[col0] = acc[mt][0][i];
+        if (tile1) orow[col1] = acc[mt][1][i];
       } else {
-        const int slot = p.sorted_slots[row0 + r];
-        tok = slot / p.K;
-        wgt = p.topk_w[slot];
+        int tok;
+        float wgt;
+        if (shared) {
+          tok = m0 + r;
+          wgt = p.shared_gate[tok];
+        } else {
+          const int slot = p.sorted_slots[row0 + r];
+          tok = slot / p.K;
+          wgt = p.topk_w[slot];
+        }
+        float* out = outf + (size_t)tok * p.out_ld;
+        atomicAdd(out + col0, wgt * acc[mt][0][i]);
+        if (tile1) atomicAdd(out + col1, wgt * acc[mt][1][i]);
       }
-      float* out = static_cast<float*>(p.out) + (size_t)tok * p.out_ld;
-      atomicAdd(out + col0, wgt * round_bf16(acc[mt][0][i]));
-      if (tile1) atomicAdd(out + col1, wgt * round_bf16(acc[mt][1][i]));
     }
   }
 }

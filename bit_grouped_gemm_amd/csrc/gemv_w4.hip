@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void k_dec_down(
             tok = slot / K;
             wgt = topk_w[slot];
           }
-          if (sl == tok) acc = __builtin_fmaf(wgt, round_bf16(part), acc);  // expert output in bf16
+          if (sl == tok) acc = __builtin_fmaf(wgt, part, acc);
         }
       }
     }

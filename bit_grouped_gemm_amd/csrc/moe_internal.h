@@ -64,8 +64,8 @@ hipError_t launch_permute(const int32_t* idx, const Dims& d, bool shared, int32_
                           const moe_plan_t& plan, hipStream_t s);
 hipError_t launch_gemm_w4(int mode, const GemmParams& p, int max_blocks, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
-hipError_t launch_combine(const uint16_t* y_perm, const int32_t* slot_pos, const float* topk_w,
-                          const uint16_t* shared_y, const float* sgate, const Dims& d, float* out,
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_pos, const float* topk_w,
+                          const float* shared_y, const float* sgate, const Dims& d, float* out,
                           hipStream_t s);
 hipError_t launch_dec_gateup(const Dims& d, const moe_layer_desc_t& desc, const uint16_t* x,
                              const moe_plan_t& plan, int max_blocks, uint16_t* a_out,
@@ -99,6 +99,10 @@ hipError_t launch_residual_rmsnorm(const float* y, float* r, uint16_t* x, int T,
                                    int init, hipStream_t s);
 hipError_t launch_debug_dequant(const moe_w4_t& w, int n_rows, int kin, int mat, int row,
                                 float* out_f32, uint16_t* out_bf16, hipStream_t s);
+hipError_t launch_mfma_loop(int workgroups, int iters, float* sink, hipStream_t s);
+double mfma_loop_flops(int workgroups, int iters);
+hipError_t launch_stream_read(const void* p, size_t bytes, int workgroups, uint32_t* sink,
+                              hipStream_t s);
 
 #ifdef __HIPCC__
 // ------------------------------------------------------------------ device helpers
@@ -121,10 +125,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
-
-// v rounded to the nearest bf16 (ties to even), as an fp32 value: an expert's output as the
-// weighted combine takes it.
-__device__ __forceinline__ float round_bf16(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 
 // Byte n of a word as fp32 (v_cvt_f32_ubyteN: one instruction).
 #define MOE_CVT_UBYTE(N)                                                   \

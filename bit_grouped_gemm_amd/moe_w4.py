@@ -26,7 +26,8 @@ EXPORTS = ("moe_status_str", "moe_version", "moe_workspace_bytes", "moe_plan_max
            "moe_route", "moe_permute", "moe_grouped_gemm_w4", "moe_combine",
            "moe_layer_forward", "moe_debug_dequant_w4", "moe_layer_num_phases",
            "moe_layer_forward_phase", "moe_residual_rmsnorm", "moe_stack_workspace_bytes",
-           "moe_stack_forward")
+           "moe_stack_forward", "moe_debug_workspace_layout", "moe_bench_mfma_loop",
+           "moe_bench_stream_read")
 
 
 class W4(ctypes.Structure):
@@ -94,6 +95,12 @@ def lib():
     L.moe_stack_forward.argtypes = [ppdesc, i32, vp, vp, i32, ctypes.c_float, vp, sz, i32, vp]
     L.moe_debug_dequant_w4.restype = ctypes.c_int
     L.moe_debug_dequant_w4.argtypes = [ctypes.POINTER(W4), i32, i32, i32, i32, vp, vp, vp]
+    L.moe_bench_mfma_loop.restype = ctypes.c_int
+    L.moe_bench_mfma_loop.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.moe_bench_stream_read.restype = ctypes.c_int
+    L.moe_bench_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    L.moe_debug_workspace_layout.restype = ctypes.c_int
+    L.moe_debug_workspace_layout.argtypes = [pdesc, i32, i32, ctypes.POINTER(sz), i32]
     _lib = L
     return L
 
@@ -247,6 +254,33 @@ def moe_debug_dequant_w4(w4: tuple, n_rows: int, kin: int, mat: int, row: int, o
     st = W4(q.data_ptr(), s.data_ptr(), b.data_ptr())
     _check(lib().moe_debug_dequant_w4(ctypes.byref(st), n_rows, kin, mat, row, _p(out_f32),
                                       _p(out_bf16), _stream(stream)), "moe_debug_dequant_w4")
+
+
+WS_REGIONS = ("logits", "topk_idx", "topk_w", "sgate", "route", "counts", "offsets",
+              "sorted_slots", "slot_pos", "blocks", "num_blocks", "a", "y", "total")
+
+
+def moe_debug_workspace_layout(layer, T: int, flags: int = 0) -> dict:
+    """Byte offsets of the workspace regions (test export), keyed by WS_REGIONS."""
+    arr = (ctypes.c_size_t * len(WS_REGIONS))()
+    _check(lib().moe_debug_workspace_layout(layer.desc_ptr, T, flags, arr, len(WS_REGIONS)),
+           "moe_debug_workspace_layout")
+    return dict(zip(WS_REGIONS, (int(v) for v in arr)))
+
+
+def moe_bench_mfma_loop(workgroups: int, iters: int, sink, stream=None) -> float:
+    """Enqueue the MFMA-loop measurement kernel; returns the flops it performs."""
+    fl = ctypes.c_double(0.0)
+    _check(lib().moe_bench_mfma_loop(workgroups, iters, _p(sink), ctypes.byref(fl),
+                                     _stream(stream)), "moe_bench_mfma_loop")
+    return fl.value
+
+
+def moe_bench_stream_read(buf, workgroups: int, sink, stream=None):
+    """Enqueue the streaming-read measurement kernel over the whole of buf."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().moe_bench_stream_read(_p(buf), nbytes, workgroups, _p(sink), _stream(stream)),
+           "moe_bench_stream_read")
 
 
 def moe_layer_num_phases(layer, T: int, flags: int = 0) -> int:

@@ -20,8 +20,9 @@
  *        + sigmoid(wg . x[t]) * Wd_s(silu(Wg_s x[t]) * (Wu_s x[t]))
  * with p = softmax over the selected router logits, ties in the top-k going to the lower
  * expert index, and every W = scale * q + bias dequantised per group of 64 inputs. The
- * inputs of the tensor operations are bf16 [P1 "The Model ..."]: the dequantised weights,
- * the SwiGLU output, and each expert's output as the weighted combine takes it.
+ * inputs of the two tensor operations of an expert are bf16 with fp32 accumulation
+ * [P1 "The Model ..."]: the dequantised weights and the SwiGLU output. Each expert's output
+ * stays fp32, and the weighted combine (a scalar-weighted sum) is computed in fp32.
  *
  * Conventions for every entry point:
  *   - bf16 values are passed as uint16_t bit patterns.
@@ -116,12 +117,18 @@ typedef struct {
 /* moe_grouped_gemm_w4 `which` */
 enum {
   MOE_GEMM_GATE_UP = 0,             /* out = A [T*K*F + T*Fs] bf16: silu(G)*U per grouped row */
-  MOE_GEMM_DOWN = 1,                /* out = Y [(T*K + T), H] bf16, unweighted, grouped rows  */
+  MOE_GEMM_DOWN = 1,                /* out = Y [(T*K + T), H] fp32, unweighted, grouped rows  */
   MOE_GEMM_DOWN_COMBINE = 2,        /* out = y [T, H] fp32, the combined layer output         */
   MOE_GEMM_DOWN_COMBINE_ATOMIC = 3  /* as 2, combined with fp32 atomics (order not fixed)     */
 };
 
-/* moe_layer_forward flags */
+/* moe_layer_forward flags. By default the prefill path (T > 16 or MOE_FLAG_FORCE_PREFILL)
+ * stores the fp32 expert outputs Y [T*K + T, H] in the workspace and then combines them in a
+ * fixed order (rank order, then the shared term): bit-reproducible. MOE_FLAG_ATOMIC_COMBINE
+ * fuses the combine into the down GEMM's epilogue with fp32 atomics instead: no Y array (a
+ * smaller workspace), but the summation order, hence the last bits of out, may vary between
+ * runs, and on gfx950 the atomics cost more time than the Y round trip they save. The decode
+ * path (T <= 16) is deterministic under every flag. */
 enum {
   MOE_FLAG_ATOMIC_COMBINE = 1,  /* prefill: fuse the combine into the down GEMM with atomics */
   MOE_FLAG_FORCE_PREFILL = 2    /* use the MFMA grouped-GEMM path even for small T           */
@@ -163,31 +170,37 @@ int moe_permute(const moe_layer_desc_t* desc, const int32_t* topk_idx, int32_t T
  *   GATE_UP: in = x [T, H] bf16 (rows gathered through plan->sorted_slots; the shared
  *            expert reads x in token order); out = A bf16, routed rows [T*K, F] in grouped
  *            order followed by shared rows [T, Fs]: A = bf16(silu(x Wg^T) * (x Wu^T)).
- *   DOWN:    in = A as above; out = Y [T*K + T, H] bf16 = bf16(A Wd^T) per grouped row
- *            (fp32 accumulation, rounded to nearest even once).
+ *   DOWN:    in = A as above; out = Y [T*K + T, H] fp32 = A Wd^T per grouped row (fp32
+ *            accumulation, not rounded).
  *   DOWN_COMBINE(_ATOMIC): in = A; out = y [T, H] fp32 =
  *            sum_k topk_w[t,k] Y[slot_pos[t*K+k]] + shared_gate[t] * Y[T*K + t]
- *            with Y the bf16-rounded rows as in DOWN, summed in fp32 (overwritten, not
- *            accumulated). Needs topk_w and, when Fs > 0, shared_gate.
+ *            with Y the fp32 rows of DOWN, summed in fp32 (overwritten, not accumulated).
+ *            Needs topk_w and, when Fs > 0, shared_gate. DOWN_COMBINE stores Y in the
+ *            workspace and adds the terms in rank order, then the shared term; _ATOMIC adds
+ *            them in the down GEMM's epilogue with fp32 atomics (no Y array).
  * For T <= 16 (and F, Fs <= 512, T*H <= 32768) GATE_UP and DOWN_COMBINE run the decode
  * path's GEMV kernels (the same ones moe_layer_forward uses for such T; DOWN_COMBINE is then
  * deterministic and needs no workspace).
- * workspace: moe_workspace_bytes(desc, T, 0) (DOWN_COMBINE stages Y in it). */
+ * workspace: moe_workspace_bytes(desc, T, 0) (DOWN_COMBINE with T > 16 stages Y in it). */
 int moe_grouped_gemm_w4(const moe_layer_desc_t* desc, int32_t which, const void* in, int32_t T,
                         const moe_plan_t* plan, const float* topk_w, const float* shared_gate,
                         void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Weighted combine [P1 "The Model ..."]: y[t] = sum_k topk_w[t,k] * y_perm[slot_pos[t*K+k]]
  *                        + shared_gate[t] * shared_y[t]     (the shared term only if Fs > 0)
- * y_perm [T*K, H] bf16 (grouped rows, as moe_grouped_gemm_w4 DOWN writes them), shared_y
- * [T, H] bf16, out [T, H] fp32 (overwritten), products and sums in fp32.
- * Deterministic: terms are added in rank order k = 0..K-1, then the shared term. */
-int moe_combine(const moe_layer_desc_t* desc, const uint16_t* y_perm, const int32_t* slot_pos,
-                const float* topk_w, const uint16_t* shared_y, const float* shared_gate,
+ * y_perm [T*K, H] fp32 (grouped rows, as moe_grouped_gemm_w4 DOWN writes them), shared_y
+ * [T, H] fp32 (rows T*K.. of that array), out [T, H] fp32 (overwritten), products and sums
+ * in fp32. Deterministic: terms are added in rank order k = 0..K-1, then the shared term. */
+int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t* slot_pos,
+                const float* topk_w, const float* shared_y, const float* shared_gate,
                 int32_t T, float* out, void* stream);
 
-/* The whole layer: x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path, larger T
- * the prefill path (MFMA grouped GEMM). For H <= 2048 and F, Fs <= 512 the decode path is three
+/* The whole layer [P1 "The Model ..."]: router (256 experts scored, 8 kept, one shared expert
+ * on every token), SwiGLU experts over 4-bit g64 weights, weighted combine -- with routing,
+ * histogram, scan, scatter and block maps on the GPU and no host synchronisation
+ * [P1 "How It Works ..."]. x [T, H] bf16 -> out [T, H] fp32. T <= 16 takes the decode path
+ * (bandwidth-bound: each selected expert's weights streamed once), larger T the prefill path
+ * (MFMA grouped GEMM with the weights rebuilt tile by tile). For H <= 2048 and F, Fs <= 512 the decode path is three
  * launches: (router logits + the shared expert's gate/up), (top-k in every workgroup + the
  * selected experts' gate/up), (down projection fused with the weighted combine); each selected
  * expert's weights are streamed once with 16-byte loads, and the combine is deterministic.
@@ -205,7 +218,7 @@ int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T
  *   decode (T <= 16, H <= 2048, F, Fs <= 512): router + shared expert; top-k + gate/up of the
  *     selected experts; down projection + combine
  *   other decode shapes: router; top-k + permutation; gate/up; down + combine
- *   prefill: router; top-k; permutation; gate/up GEMM; down GEMM; combine
+ *   prefill: router; top-k; permutation; gate/up GEMM; down GEMM storing Y; combine
  *     (MOE_FLAG_ATOMIC_COMBINE: ...; gate/up GEMM; zero fill of out; down GEMM + combine). */
 int32_t moe_layer_num_phases(const moe_layer_desc_t* desc, int32_t T, int32_t flags);
 int moe_layer_forward_phase(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T,
@@ -242,6 +255,40 @@ int moe_stack_forward(const moe_layer_desc_t* const* layers, int32_t n_layers, f
  * as computed in fp32, out_bf16 [Kin] its bf16 rounding (either may be NULL). */
 int moe_debug_dequant_w4(const moe_w4_t* w, int32_t n_rows, int32_t Kin, int32_t mat,
                          int32_t row, float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* Test export: byte offsets of the workspace regions that moe_layer_forward_phase leaves for
+ * the next phase, so that a test can check each launch on its own. offsets[i] receives, for
+ * T tokens and these flags, the offset of region i in this order:
+ *   0 logits   router logits [T, E] fp32 then the shared-gate logits [T] (decode path), or
+ *              up to 8 split-K partial slices [T, E+1] (prefill path)
+ *   1 topk_idx [T, K] int32      2 topk_w [T, K] fp32        3 sgate [T] fp32
+ *   4 route    decode route record, int32 words: D, expert[T*K], rows[T*K], first grouped
+ *              row[T*K], token mask[T*K], routing weight per grouped row[T*K] (fp32),
+ *              shared gate[T] (fp32); D entries in ascending expert order (T = 1: rank order)
+ *   5 counts [E]   6 offsets [E+1]   7 sorted_slots [T*K]   8 slot_pos [T*K]
+ *   9 blocks [max_blocks*4]   10 num_blocks [1]
+ *   11 A [T*K*F + T*Fs] bf16 (grouped routed rows, then the shared rows)
+ *   12 Y [T*K + T, H] fp32 (not with MOE_FLAG_ATOMIC_COMBINE: then equal to the total)
+ *   13 total bytes (= moe_workspace_bytes)
+ * n: entries of offsets (at most 14 are written). Returns MOE_OK, or an error as
+ * moe_workspace_bytes would return 0. */
+int moe_debug_workspace_layout(const moe_layer_desc_t* desc, int32_t T, int32_t flags,
+                               size_t* offsets, int32_t n);
+
+/* Measurement export: enqueues `workgroups` workgroups of four waves, each wave issuing
+ * iters x 8 independent bf16 MFMAs (32x32x16, fp32 accumulation) on register operands, and
+ * writes the flops that launch performs to *flops. Timed by the caller (events on `stream`), it
+ * gives the dense bf16 matrix rate the chip sustains, beside the datasheet peak. sink: device
+ * buffer of workgroups*256 floats, written only in an impossible case (keeps the loop alive). */
+int moe_bench_mfma_loop(int32_t workgroups, int32_t iters, float* sink, double* flops,
+                        void* stream);
+
+/* Measurement export: reads `bytes` (a multiple of 16) of the device buffer p once with 16-byte
+ * loads over `workgroups` workgroups of 256 threads (four loads in flight per thread). Timed by
+ * the caller, it gives the HBM read rate a streaming kernel reaches. sink: device buffer of
+ * workgroups*256 uint32, written only in an impossible case. */
+int moe_bench_stream_read(const void* p, size_t bytes, int32_t workgroups, uint32_t* sink,
+                          void* stream);
 
 #ifdef __cplusplus
 }

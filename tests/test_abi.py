@@ -66,8 +66,11 @@ def test_workspace_sizes():
     d = fake_desc()
     base = ws_bytes(d, 4096)
     atomic = ws_bytes(d, 4096, M.MOE_FLAG_ATOMIC_COMBINE)
-    # the unfused combine stages bf16 rows for T*K + T grouped rows
-    assert base - atomic >= (4096 * 8 + 4096) * 2048 * 2  # the bf16 expert outputs
+    # the default (deterministic) combine stages fp32 expert outputs for T*K + T grouped rows;
+    # the fused atomic combine needs none
+    assert base - atomic >= (4096 * 8 + 4096) * 2048 * 4
+    # unknown flag bits are rejected
+    assert ws_bytes(d, 4096, 4) == 0 and ws_bytes(d, 4096, 8) == 0
     assert ws_bytes(d, 1) < ws_bytes(d, 8) < base
     assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 4096) == 32768 // M.MOE_BLOCK_M + 256 + 4096 // M.MOE_BLOCK_M
     assert M.lib().moe_plan_max_blocks(ctypes.byref(d), 1) == 1 + 8 + 1
@@ -133,3 +136,24 @@ def test_call_rejections_before_launch():
     assert L.moe_debug_dequant_w4(ctypes.byref(w), 4, 96, 0, 0, FAKE, None, None) \
         == M.MOE_UNSUPPORTED
 
+
+
+def test_workspace_layout_export():
+    """The test export reports the regions in order, inside the workspace size."""
+    import ctypes as C
+    d = fake_desc()
+    for T, flags in ((1, 0), (8, 0), (4096, 0), (4096, M.MOE_FLAG_ATOMIC_COMBINE)):
+        arr = (C.c_size_t * len(M.WS_REGIONS))()
+        assert M.lib().moe_debug_workspace_layout(C.byref(d), T, flags, arr, len(arr)) == M.MOE_OK
+        off = list(arr)
+        assert off[-1] == ws_bytes(d, T, flags)
+        assert off == sorted(off) and all(o % 256 == 0 for o in off)
+        # A holds T*K*F + T*Fs bf16 values, Y (deterministic only) (T*K + T)*H fp32
+        a, y, total = off[M.WS_REGIONS.index("a")], off[M.WS_REGIONS.index("y")], off[-1]
+        assert y - a >= (T * 8 * 512 + T * 512) * 2
+        if flags & M.MOE_FLAG_ATOMIC_COMBINE:
+            assert total == y
+        else:
+            assert total - y >= (T * 8 + T) * 2048 * 4
+    arr = (C.c_size_t * 14)()
+    assert M.lib().moe_debug_workspace_layout(C.byref(d), 4, 4, arr, 14) == M.MOE_INVALID_ARG

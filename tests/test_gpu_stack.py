@@ -16,12 +16,13 @@ from oracle import moe_oracle as O
 pytestmark = pytest.mark.gpu
 
 FORCE = 2
+ATOMIC = 1
 
 
 @pytest.mark.parametrize("name,T,flags", [("full", 1, 0), ("full", 8, 0), ("mid", 13, 0),
-                                          ("mid", 300, 0), ("odd", 130, 0), ("odd", 16, FORCE),
-                                          ("full", 16, 0), ("wide", 4, 0), ("many", 1, 0),
-                                          ("many", 40, 0)])
+                                          ("mid", 300, 0), ("odd", 130, 0),
+                                          ("odd", 16, FORCE), ("full", 16, 0), ("wide", 4, 0),
+                                          ("many", 1, 0), ("many", 40, 0), ("mid", 300, ATOMIC)])
 def test_phases_reproduce_forward(name, T, flags):
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
@@ -38,7 +39,10 @@ def test_phases_reproduce_forward(name, T, flags):
     for ph in range(n):
         M.moe_layer_forward_phase(layer, x, out, ws2, ph, flags)
     torch.cuda.synchronize()
-    assert torch.equal(out, ref)
+    if flags & ATOMIC:   # summation order not fixed
+        assert O.error_stats(out.cpu().numpy(), ref.cpu().numpy())["max_rel"] < 1e-5
+    else:
+        assert torch.equal(out, ref)
     with pytest.raises(M.MoEError):
         M.moe_layer_forward_phase(layer, x, out, ws2, n, flags)
 
@@ -118,6 +122,20 @@ def test_stack_matches_layerwise_and_oracle(name, T, nl):
     stack.forward(resid, x, ws)
     torch.cuda.synchronize()
     assert torch.equal(resid, r_lw) and torch.equal(x, x_lw)
+    if T > 16:
+        # the atomic combine: its summation order is not fixed, and each layer's
+        # input is re-rounded to bf16, so a last-bit difference can move an input by one bf16
+        # step and grow over the layers; each layer is therefore checked against the oracle on
+        # its own input, and the stack call against the layer-wise run within the parity bar
+        _, r_at, _ = _layerwise(layers_dev, layers_host, name, T, ATOMIC, stream=50)
+        ws0 = stack.alloc_workspace(T, ATOMIC)
+        x0 = torch.from_numpy(xh.view(np.int16)).to(DEV)
+        r0 = torch.empty_like(resid)
+        stack.forward(r0, x0, ws0, ATOMIC)
+        torch.cuda.synchronize()
+        st = O.error_stats(r0.cpu().numpy(), r_at.cpu().numpy())
+        log(f"[stack] atomic-combine stack vs its layer-wise run: {st}")
+        assert st["max_rel"] <= TOL_MAX_REL and st["mean_abs"] <= TOL_MEAN_ABS
 
 
 def test_stack_of_small_layers_end_to_end():
@@ -146,3 +164,62 @@ def test_stack_of_small_layers_end_to_end():
     log(f"[stack] tiny end-to-end: resid {st} | next input {sx}")
     assert st["max_rel"] <= TOL_MAX_REL and st["mean_abs"] <= TOL_MEAN_ABS
     assert sx["max_rel"] <= TOL_MAX_REL and sx["mean_abs"] <= TOL_MEAN_ABS
+
+
+def test_stack_prefill_then_fed_back_decode_steps():
+    """A 64-token prefill chunk through two full-size layers (every token checked, layer by
+    layer), then 8 decode steps whose input is the previous step's normalised output left on
+    the device ([P1 "How It Works ..."]: the next step's input stays GPU-resident). Each step is
+    checked layer by layer against the oracle on the GPU's own input, and the stack call must
+    give the layer-by-layer composition bit for bit, step after step."""
+    import torch
+    from bit_grouped_gemm_amd import moe_w4 as M
+    name, nl = "full", 2
+    layers_dev = [device_layer(name, 0, l) for l in range(nl)]
+    layers_host = [host_layer(name, 0, l) for l in range(nl)]
+    log("[stack] prefill chunk T=64, 2 layers, every token")
+    xh, r_lw, x_lw = _layerwise(layers_dev, layers_host, name, 64, 0, stream=70)
+    stack = M.Stack(layers_dev)
+    ws = stack.alloc_workspace(64)
+    x = torch.from_numpy(xh.view(np.int16)).to(DEV)
+    resid = torch.empty((64, layers_dev[0].H), dtype=torch.float32, device=DEV)
+    stack.forward(resid, x, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(resid, r_lw) and torch.equal(x, x_lw)
+    # decode: the first step takes the prefill's last normalised row, then each step its own
+    x_step = x[63:64].clone()
+    ws1 = stack.alloc_workspace(1)
+    r1 = torch.empty((1, layers_dev[0].H), dtype=torch.float32, device=DEV)
+    for step in range(8):
+        log(f"[stack] decode step {step}")
+        _, r_ref, x_ref = _layerwise_from(layers_dev, layers_host, name, x_step.clone(), step)
+        xs = x_step.clone()
+        stack.forward(r1, xs, ws1)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, r_ref) and torch.equal(xs, x_ref), step
+        x_step = xs
+
+
+def _layerwise_from(layers_dev, layers_host, name, x, tag):
+    """_layerwise for a device input x [T, H] bf16 (updated in place to the next input)."""
+    import torch
+    from bit_grouped_gemm_amd import moe_w4 as M
+    s = synth.SHAPES[name]
+    T = x.shape[0]
+    resid = torch.empty((T, s.H), dtype=torch.float32, device=DEV)
+    M.moe_residual_rmsnorm(None, resid, x, init=True)
+    y = torch.empty((T, s.H), dtype=torch.float32, device=DEV)
+    for l, (ld, lh) in enumerate(zip(layers_dev, layers_host)):
+        ws = M.alloc_workspace(ld, T)
+        M.moe_layer_forward(ld, x, y, ws)
+        torch.cuda.synchronize()
+        x_in = u16(x)
+        gidx = gpu_routing(ld, x, T)
+        ref, _, ties, swapped = oracle_reference(name, lh, x_in, s.K, gpu_idx=gidx)
+        st = O.error_stats(y.cpu().numpy(), ref)
+        log(f"[stack]   step {tag} layer {l}: max_rel={st['max_rel']:.3e} "
+            f"mean_abs={st['mean_abs']:.3e} near-ties={len(ties)} rerouted={swapped}")
+        assert st["max_rel"] <= TOL_MAX_REL and st["mean_abs"] <= TOL_MEAN_ABS, (l, st)
+        M.moe_residual_rmsnorm(y, resid, x)
+    torch.cuda.synchronize()
+    return None, resid, x

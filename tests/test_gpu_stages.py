@@ -44,19 +44,21 @@ def test_grouped_gemm_stages(name, T):
     TK = T * K
     a = torch.empty(TK * F + T * Fs, dtype=torch.int16, device=DEV)
     M.moe_grouped_gemm_w4(layer, M.MOE_GEMM_GATE_UP, x, T, plan, None, None, a, ws)
-    y = torch.empty((TK + T) * H, dtype=torch.int16, device=DEV)  # bf16 expert outputs
+    y = torch.empty((TK + T) * H, dtype=torch.float32, device=DEV)  # fp32 expert outputs
     M.moe_grouped_gemm_w4(layer, M.MOE_GEMM_DOWN, a, T, plan, None, None, y, ws)
     out_c = torch.empty(T * H, dtype=torch.float32, device=DEV)
     M.moe_grouped_gemm_w4(layer, M.MOE_GEMM_DOWN_COMBINE, a, T, plan, w, sg, out_c, ws)
     out_a = torch.empty(T * H, dtype=torch.float32, device=DEV)
     M.moe_grouped_gemm_w4(layer, M.MOE_GEMM_DOWN_COMBINE_ATOMIC, a, T, plan, w, sg, out_a, ws)
+    out_m = torch.empty(T * H, dtype=torch.float32, device=DEV)
+    M.moe_combine(layer, y, plan["slot_pos"], w, y[TK * H:] if Fs else None, sg, T, out_m)
     torch.cuda.synchronize()
 
     xf = O.bf16_to_f64(xh)
     sorted_slots = plan["sorted_slots"].cpu().numpy()[:TK]
     offsets = plan["offsets"].cpu().numpy()
     A = O.bf16_to_f64(u16(a))
-    Y = O.bf16_to_f64(u16(y)).reshape(TK + T, H)
+    Y = y.cpu().numpy().astype(np.float64).reshape(TK + T, H)
     # gate/up + SwiGLU, per grouped row; then down on the library's own A
     a_ref = np.empty_like(A)
     y_ref = np.empty((TK + T, H))
@@ -81,37 +83,34 @@ def test_grouped_gemm_stages(name, T):
             a_ref[base + rows[:, None] * Fs + np.arange(Fs)] = ar
             a_rows = A[base + rows[:, None] * Fs + np.arange(Fs)]
             y_ref[TK + rows] = a_rows @ wd.T
-    # A is the bf16 rounding of silu(G)*U; G and U carry fp32 accumulation error, so a value
-    # may round to the neighbouring bf16 (one ulp, 2^-7 relative at most), and values that
-    # nearly cancel may differ by the accumulation error itself (bounded via the row scale).
-    mism = np.mean(A != a_ref)
-    scale = np.abs(a_ref).max()
-    excess = np.abs(A - a_ref) - (2.0 ** -7 * np.abs(a_ref) + 1e-5 * scale)
-    log(f"[stages]   A: {mism:.2e} of values differ from RNE(exact), worst excess {excess.max():.2e}")
-    assert mism < 5e-3 and excess.max() <= 0
-    # Y is the bf16 rounding of the fp32-accumulated down product: within half a bf16 step
-    # (2^-8 relative) of the exact product, plus the accumulation error near a midpoint
-    mism = np.mean(Y != O.round_to_bf16(y_ref))
-    excess = np.abs(Y - y_ref) - (2.0 ** -8 * np.abs(y_ref) + 1e-5 * np.abs(y_ref).max())
-    log(f"[stages]   Y: {mism:.2e} of values differ from RNE(exact), worst excess {excess.max():.2e}")
-    assert mism < 5e-3 and excess.max() <= 0
-    # combine from the library's weights and its own bf16 Y
+    check_a(A, a_ref, "A")
+    # Y is the fp32-accumulated down product of the library's own A: within the fp32
+    # accumulation error of the exact product (relative to the row's scale)
+    st = O.error_stats(Y, y_ref)
+    log(f"[stages]   Y vs exact product of the library's A: {st}")
+    assert st["max_rel"] < 1e-5
+    # combine from the library's weights and its own fp32 Y; every path sums fp32 terms
     wh = w.cpu().numpy().reshape(T, K)
     sgh = sg.cpu().numpy()
     slot_pos = plan["slot_pos"].cpu().numpy()[:TK].reshape(T, K)
     comb = np.einsum("tk,tkh->th", wh.astype(np.float64), Y[slot_pos])
     if Fs:
         comb += sgh[:, None] * Y[TK:]
-    # The atomic path and the prefill path of DOWN_COMBINE round the same fp32 products as
-    # DOWN, so only the fp32 sums differ; for T <= 16 DOWN_COMBINE runs the decode GEMV, whose
-    # own accumulation order may round an expert output to the neighbouring bf16 (2^-7 of
-    # that term at most).
-    gemv = T <= 16
-    for tag, o, tol in (("deterministic", out_c, 2.0 ** -7 if gemv else 1e-5),
-                        ("atomic", out_a, 1e-5)):
+    for tag, o in (("deterministic", out_c), ("atomic", out_a), ("moe_combine", out_m)):
         st = O.error_stats(o.cpu().numpy().reshape(T, H), comb)
         log(f"[stages]   combine {tag}: {st}")
-        assert st["max_rel"] < tol
+        assert st["max_rel"] < 1e-5
+
+
+def check_a(A, a_ref, what):
+    """A is the bf16 rounding of silu(G)*U; G and U carry fp32 accumulation error, so a value
+    may round to the neighbouring bf16 (one ulp, 2^-7 relative at most), and values that nearly
+    cancel may differ by the accumulation error itself (bounded via the row scale)."""
+    mism = np.mean(A != a_ref)
+    scale = np.abs(a_ref).max()
+    excess = np.abs(A - a_ref) - (2.0 ** -7 * np.abs(a_ref) + 1e-5 * scale)
+    log(f"[stages]   {what}: {mism:.2e} of values differ from RNE(exact), worst excess {excess.max():.2e}")
+    assert mism < 5e-3 and excess.max() <= 0
 
 
 def test_combine_entry_point():
@@ -120,16 +119,15 @@ def test_combine_entry_point():
     layer = device_layer("mid")
     T, K, H = 77, layer.K, layer.H
     rng = np.random.default_rng(0)
-    y_perm = O.round_to_bf16(rng.normal(size=(T * K, H)))   # bf16 expert outputs
-    sh_y = O.round_to_bf16(rng.normal(size=(T, H)))
+    y_perm = rng.normal(size=(T * K, H)).astype(np.float32)   # fp32 expert outputs
+    sh_y = rng.normal(size=(T, H)).astype(np.float32)
     wts = rng.random((T, K)).astype(np.float32)
     sgt = rng.random(T).astype(np.float32)
     slot_pos = rng.permutation(T * K).astype(np.int32)
     d = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
     out = torch.empty(T * H, dtype=torch.float32, device=DEV)
-    M.moe_combine(layer, d(O.bf16_bits(y_perm).view(np.int16)), d(slot_pos), d(wts),
-                  d(O.bf16_bits(sh_y).view(np.int16)), d(sgt), T, out)
+    M.moe_combine(layer, d(y_perm), d(slot_pos), d(wts), d(sh_y), d(sgt), T, out)
     torch.cuda.synchronize()
     ref = np.einsum("tk,tkh->th", wts.astype(np.float64),
-                    y_perm[slot_pos.reshape(T, K)]) + sgt[:, None] * sh_y
+                    y_perm.astype(np.float64)[slot_pos.reshape(T, K)]) + sgt[:, None] * sh_y
     assert O.error_stats(out.cpu().numpy().reshape(T, H), ref)["max_rel"] < 1e-6
