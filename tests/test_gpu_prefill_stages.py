@@ -40,20 +40,24 @@ def _w(proj, e):
     return _deq32(proj, e).astype(np.float64)
 
 
+FORCE = 2
+
+
 @pytest.mark.parametrize("name,T", [("full_skew", 512), ("full", 512), ("full", 4096),
-                                    ("full_skew", 4096)])
+                                    ("full_skew", 4096), ("full", 8), ("full", 64)])
 def test_prefill_gemms_every_row(name, T):
     import torch
     from bit_grouped_gemm_amd import moe_w4 as M
-    log(f"[pre-stages] {name} T={T}")
+    flags = FORCE if T <= 16 else 0   # small T: the MFMA path forced
+    log(f"[pre-stages] {name} T={T} flags={flags}")
     layer = device_layer(name)
     H, E, K, F, Fs = layer.H, layer.E, layer.K, layer.F, layer.Fs
     TK = T * K
     xh, x = tokens(name, T, stream=40)
-    lay = M.moe_debug_workspace_layout(layer, T)
+    lay = M.moe_debug_workspace_layout(layer, T, flags)
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device=DEV)
     out = torch.full((T, H), float("nan"), dtype=torch.float32, device=DEV)
-    M.moe_layer_forward(layer, x, out, ws)
+    M.moe_layer_forward(layer, x, out, ws, flags)
     torch.cuda.synchronize()
 
     def region(key, n, dtype):
@@ -69,6 +73,22 @@ def test_prefill_gemms_every_row(name, T):
     A = O.bf16_to_f64(region("a", TK * F + T * Fs, np.uint16))
     Y = region("y", (TK + T) * H, np.float32).astype(np.float64).reshape(TK + T, H)
     counts = np.diff(offsets)
+    # the prefill router and top-k: indices as the oracle's (near-tie tokens: a tie-equivalent
+    # set), weights and shared gates to fp32 accuracy
+    host = host_layer(name)
+    idx = region("topk_idx", TK, np.int32).reshape(T, K)
+    logits = O.router_logits(xh, host["router_w"], host["router_bias"])
+    ridx, rp = O.select_topk(logits, K)
+    ties = set(O.near_ties(logits, K).tolist())
+    same = np.all(idx == ridx, axis=1)
+    assert all(t in ties for t in np.nonzero(~same)[0]), "selection differs without a near-tie"
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    werr = np.abs(topk_w - z / z.sum(axis=1, keepdims=True)).max()
+    gerr = np.abs(sgate - O.shared_gate(xh, host["shared_gate_w"])).max()
+    log(f"[pre-stages]   router: {int((~same).sum())} tokens rerouted ({len(ties)} near-ties), "
+        f"weights max abs error {werr:.2e}, shared gate {gerr:.2e}")
+    assert werr <= 5e-6 and gerr <= 2e-6
     tall = int((blocks[:, 2] == M.MOE_BLOCK_M).sum())
     log(f"[pre-stages]   {nblk} blocks ({tall} of {M.MOE_BLOCK_M} rows), "
         f"{int((counts == 0).sum())} empty experts, max {counts.max()} rows")
@@ -99,9 +119,9 @@ def test_prefill_gemms_every_row(name, T):
     assert st["max_rel"] < 1e-5
 
     # the atomic combine on the same plan: the same output within fp32 summation noise
-    ws0 = M.alloc_workspace(layer, T, ATOMIC)
+    ws0 = M.alloc_workspace(layer, T, ATOMIC | flags)
     out0 = torch.empty_like(out)
-    M.moe_layer_forward(layer, x, out0, ws0, ATOMIC)
+    M.moe_layer_forward(layer, x, out0, ws0, ATOMIC | flags)
     torch.cuda.synchronize()
     st = O.error_stats(out0.cpu().numpy(), comb)
     log(f"[pre-stages]   atomic combine vs fp64 sum of the library's Y: {st}")
