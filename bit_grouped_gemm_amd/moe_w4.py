@@ -27,7 +27,8 @@ EXPORTS = ("moe_status_str", "moe_version", "moe_workspace_bytes", "moe_plan_max
            "moe_layer_forward", "moe_debug_dequant_w4", "moe_layer_num_phases",
            "moe_layer_forward_phase", "moe_residual_rmsnorm", "moe_stack_workspace_bytes",
            "moe_stack_forward", "moe_debug_workspace_layout", "moe_bench_mfma_loop",
-           "moe_bench_stream_read")
+           "moe_bench_stream_read", "moe_layer_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class W4(ctypes.Structure):
@@ -82,6 +83,8 @@ def lib():
     L.moe_combine.argtypes = [pdesc, vp, vp, vp, vp, vp, i32, vp, vp]
     L.moe_layer_forward.restype = ctypes.c_int
     L.moe_layer_forward.argtypes = [pdesc, vp, i32, vp, vp, sz, i32, vp]
+    L.moe_layer_forward_noalloc.restype = ctypes.c_int
+    L.moe_layer_forward_noalloc.argtypes = [pdesc, vp, i32, vp, i32, vp]
     L.moe_layer_num_phases.restype = i32
     L.moe_layer_num_phases.argtypes = [pdesc, i32, i32]
     L.moe_layer_forward_phase.restype = ctypes.c_int
@@ -248,6 +251,12 @@ def moe_layer_forward(layer, x, out, workspace, flags: int = 0, stream=None):
                                    workspace.numel(), flags, _stream(stream)), "moe_layer_forward")
 
 
+def moe_layer_forward_noalloc(layer, x, out, flags: int = 0, stream=None):
+    """moe_layer_forward with the library's own per-GPU scratch array (no workspace argument)."""
+    _check(lib().moe_layer_forward_noalloc(layer.desc_ptr, _p(x), x.shape[0], _p(out), flags,
+                                           _stream(stream)), "moe_layer_forward_noalloc")
+
+
 def moe_debug_dequant_w4(w4: tuple, n_rows: int, kin: int, mat: int, row: int, out_f32=None,
                          out_bf16=None, stream=None):
     q, s, b = w4
@@ -280,7 +289,8 @@ def moe_bench_stream_read(buf, workgroups: int, sink, stream=None):
     """Enqueue the streaming-read measurement kernel over the whole of buf."""
     nbytes = buf.numel() * buf.element_size()
     _check(lib().moe_bench_stream_read(_p(buf), nbytes, workgroups, _p(sink), _stream(stream)),
-           "moe_bench_stream_read")
+           "moe_bench_stream_read", "moe_layer_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_layer_num_phases(layer, T: int, flags: int = 0) -> int:

@@ -209,6 +209,24 @@ int moe_combine(const moe_layer_desc_t* desc, const float* y_perm, const int32_t
 int moe_layer_forward(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T, float* out,
                       void* workspace, size_t ws_bytes, int32_t flags, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code under HIP-graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * scratch memory taken from a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that each GPU the library runs on holds until the process ends. 64 MiB covers every decode
+ * batch and a 512-token prefill chunk of the full-size layer (moe_workspace_bytes gives what a
+ * call needs). The call allocates nothing (no hipMalloc, no allocating library routine); it
+ * looks up the array's device address once per GPU (hipGetSymbolAddress, on the first call
+ * on that device).
+ *   Returns MOE_WORKSPACE_TOO_SMALL if moe_workspace_bytes(desc, T, flags) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES, MOE_HIP_ERROR if the array's address cannot be obtained, and
+ *   otherwise what moe_layer_forward returns.
+ *   All calls on one GPU share its array, which keeps the last call's contents (no kernel
+ *   needs it cleared): calls that may overlap on one GPU (several streams or host threads)
+ *   race and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_layer_desc_t* desc, const uint16_t* x, int32_t T,
+                              float* out, int32_t flags, void* stream);
+
 /* moe_layer_forward as its sequence of kernel launches, one launch per call, for measuring
  * and checking the kernels one at a time. moe_layer_num_phases(desc, T, flags) gives the
  * number of launches for this T and these flags (0 if the arguments are invalid); calling
