@@ -1,2 +1,3 @@
-"""fp64 CPU oracle for the MoE layer (test infrastructure only; see moe_oracle's header)."""
-from . import moe_oracle  # noqa: F401
+"""fp64 CPU oracles (test infrastructure only; see each module's header): the MoE layer, GQA
+decode attention over a block-paged KV cache, and the gated delta-rule recurrence."""
+from . import attn_oracle, delta_oracle, moe_oracle  # noqa: F401
