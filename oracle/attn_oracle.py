@@ -23,7 +23,7 @@ physical block block_table[b, j // BS].
 Readings where the pages are silent (also listed in the design notes): the head size is not
 given (the model's hidden size divided by the 16 query heads, 128, is the default workload);
 the softmax scale is a parameter (1/sqrt(D) by default); the output is fp32; q, K and V are
-bf16 values taken exactly.
+bf16 values taken exactly; a sequence with no tokens has an empty sum and a zero output.
 """
 from __future__ import annotations
 
@@ -49,6 +49,8 @@ def attention(q, k, v, scale: float) -> np.ndarray:
     Hq, Hkv = q.shape[0], k.shape[0]
     G = Hq // Hkv
     out = np.empty_like(q)
+    if k.shape[1] == 0:          # no keys: the weighted sum is empty
+        return np.zeros_like(q)
     for h in range(Hq):
         g = h // G
         s = scale * (k[g] @ q[h])

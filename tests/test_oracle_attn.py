@@ -128,6 +128,12 @@ def test_weights_sum_to_one_and_output_is_a_convex_combination():
     assert np.allclose(out2, 2 * out + 1, rtol=1e-12, atol=1e-12)
 
 
+def test_empty_sequence_gives_zero():
+    q = np.ones((4, 8))
+    out = A.attention(q, np.zeros((2, 0, 8)), np.zeros((2, 0, 8)), 0.5)
+    assert out.shape == (4, 8) and np.all(out == 0)
+
+
 def test_generator_layout():
     shape = synth.ATTN_SHAPES["full"]
     q, kc, vc, table, lens = synth.make_attn_inputs(shape, [100, 1, 64], seed=0)
