@@ -1,0 +1,371 @@
+// Grouped-query decode attention over a block-paged KV cache, and its C ABI (attn_gqa.h).
+//
+// "Perplexity's Lily: A Breakthrough Local Inference Engine Tailored Exclusively for Apple
+// Silicon": section "The Model: Qwen3.6-35B-A3B in Focus" (grouped-query attention, 16 query
+// heads sharing two KV heads, over a growing key-value cache) and section "How It Works: Prefill
+// and Decode Strategies" (coalesced key and value cache reads; GQA packing, i.e. the query heads
+// of a KV head sharing its reads; a fixed-block cache layout). Decode attention reads every cached
+// key and value once per token and does a few flops per byte: it is bound by HBM bandwidth, so
+// the work is plain fp32 VALU arithmetic (dot2 on bf16 pairs), not MFMA.
+//
+// Layout of the work (split over the context, then a merge):
+//  * k_attn_split: one workgroup of 4 waves per (sequence, KV head, chunk of the context) with
+//    all G query heads of that KV head (packed). A token's key row of D bf16 is read by D/8
+//    consecutive lanes, 16 bytes each, so one wave instruction reads whole rows (64 * 16 bytes);
+//    the block table is read per token, so chunks may span blocks of any placement. Scores of
+//    the chunk go to LDS, then each head's maximum and exponentials (fp32), then P.V with each
+//    lane accumulating 8 dimensions of G heads; the chunk's (max, sum, acc) per head is stored.
+//  * k_attn_combine: per (sequence, query head), the chunks' results are merged in chunk order
+//    (rescaled by exp(max_c - max)), so the output does not depend on scheduling.
+#include <cmath>
+
+#include "attn_gqa.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnLdsMax = 64 * 1024;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* table;
+  const int32_t* lens;
+  float* part;  // [B, Hq, nchunks, D + 4]: max, sum, -, -, acc[D]
+  float* out;   // [B, Hq, D]
+  int Hq, Hkv, bs_shift, MB, nblocks, max_len, chunk, nchunks;
+  float scale;
+};
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of a group ends with the
+// group's total. Distances below 16 use DPP partners inside a row of 16 lanes.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (N >= 16) v += dpp_partner16<8>(v);
+  v += dpp_partner16<4>(v);
+  v += dpp_partner16<2>(v);
+  v += dpp_partner16<1>(v);
+  return v;
+}
+
+}  // namespace
+
+// HPW query heads per workgroup (G when packed, 1 when not); D head size.
+template <int D, int HPW>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
+  constexpr int LPT = D / 8;     // lanes per token row (16 bytes each)
+  constexpr int TPI = 64 / LPT;  // tokens per wave instruction
+  constexpr int TPB = 4 * TPI;   // tokens per workgroup step
+  constexpr int U = 4;           // steps whose rows are requested before the first is used
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = a.chunk, c0 = blockIdx.x * C, b = blockIdx.z;
+  const int h0 = blockIdx.y * HPW;           // first query head of the workgroup
+  const int g = h0 / (a.Hq / a.Hkv);         // its KV head
+  int len = a.lens[b];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int n = min(C, len - c0);            // tokens of this chunk
+  if (n <= 0) return;                        // past the sequence: the merge reads no record here
+  float* sc = sm;                            // scores, then probabilities [HPW][C]
+  float* wacc = sm + HPW * C;                // per-wave sums [4][HPW][D]
+  float* ml = wacc + 4 * HPW * D;            // [2][HPW] max and sum
+
+  const int dsl = lane % LPT, tsub = lane / LPT;
+  uint4 qv[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
+  const int32_t* trow = a.table + (size_t)b * a.MB;
+  const int bs_mask = (1 << a.bs_shift) - 1;
+  // this lane's 16 bytes of token s of the chunk (s < n)
+  auto row = [&](const uint16_t* cache, int s) -> const uint4* {
+    const int j = c0 + s;
+    int blk = trow[j >> a.bs_shift];
+    blk = blk < 0 ? 0 : (blk >= a.nblocks ? a.nblocks - 1 : blk);
+    return reinterpret_cast<const uint4*>(
+        cache + ((((size_t)blk * a.Hkv + g) << a.bs_shift) + (j & bs_mask)) * D + dsl * 8);
+  };
+
+  // ---- scores: q_h . k_j for the chunk's tokens, scaled
+  for (int s0 = 0; s0 < n; s0 += U * TPB) {
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * TPB + wave * TPI + tsub;
+      kv[u] = *row(a.kc, s < n ? s : n - 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * TPB + wave * TPI + tsub;
+      float t[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
+        d = dot2_bf16(kv[u].y, qv[hh].y, d);
+        d = dot2_bf16(kv[u].z, qv[hh].z, d);
+        d = dot2_bf16(kv[u].w, qv[hh].w, d);
+        t[hh] = group_sum<LPT>(d);
+      }
+      float val = 0.0f;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+        if (dsl == hh) val = t[hh];
+      if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
+    }
+  }
+  __syncthreads();
+
+  // ---- per head: maximum, exponentials (kept in place) and their sum
+  for (int hh = wave; hh < HPW; hh += 4) {
+    float* sh = sc + hh * C;
+    float m = -INFINITY;
+    for (int i = lane; i < n; i += 64) m = fmaxf(m, sh[i]);
+    m = wave_max_f(m);
+    float l = 0.0f;
+    for (int i = lane; i < n; i += 64) {
+      const float p = __expf(sh[i] - m);
+      sh[i] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      ml[hh] = m;
+      ml[HPW + hh] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- P.V: each lane accumulates its 8 dimensions for the HPW heads
+  float acc[HPW][8];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += U * TPB) {
+    uint4 vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * TPB + wave * TPI + tsub;
+      vv[u] = *row(a.vc, s < n ? s : n - 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * TPB + wave * TPI + tsub;
+      if (s < n) {
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+          v8[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const float p = sc[hh * C + s];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, v8[e], acc[hh][e]);
+        }
+      }
+    }
+  }
+  // sum over the wave's token groups (lanes with the same dimensions), then over the waves
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1)
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off, 64);
+  if (tsub == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[(wave * HPW + hh) * D + dsl * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  const size_t rec = (size_t)(D + 4);
+  float* part = a.part + (((size_t)b * a.Hq + h0) * a.nchunks + blockIdx.x) * rec;
+  for (int i = tid; i < HPW * D; i += kAttnThreads) {
+    const int hh = i / D, d = i % D;
+    const float s = ((wacc[hh * D + d] + wacc[(HPW + hh) * D + d]) + wacc[(2 * HPW + hh) * D + d]) +
+                    wacc[(3 * HPW + hh) * D + d];
+    part[hh * a.nchunks * rec + 4 + d] = s;
+  }
+  if (tid < HPW) {
+    part[tid * a.nchunks * rec + 0] = ml[tid];
+    part[tid * a.nchunks * rec + 1] = ml[HPW + tid];
+  }
+}
+
+// One wave per (query head, sequence): the chunks' records merged in chunk order.
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  int len = a.lens[b];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int nc = (len + a.chunk - 1) / a.chunk;
+  float* o = a.out + ((size_t)b * a.Hq + h) * D;
+  if (nc == 0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[lane + 64 * i] = 0.0f;
+    return;
+  }
+  const size_t rec = (size_t)(D + 4);
+  const float* r = a.part + ((size_t)b * a.Hq + h) * a.nchunks * rec;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, r[c * rec]);
+  float L = 0.0f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+  for (int c = 0; c < nc; ++c) {
+    const float w = __expf(r[c * rec] - M);
+    L = __builtin_fmaf(w, r[c * rec + 1], L);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, r[c * rec + 4 + lane + 64 * i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[lane + 64 * i] = acc[i] / L;
+}
+
+// ------------------------------------------------------------------------------ host side
+namespace {
+
+bool attn_desc_ok(const attn_gqa_desc_t* d) {
+  if (!d || d->num_q_heads <= 0 || d->num_kv_heads <= 0) return false;
+  if (d->num_q_heads % d->num_kv_heads) return false;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return false;
+  const int bs = d->block_size;
+  return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
+}
+
+struct AttnPlan {
+  int hpw, chunk, nchunks;
+  size_t lds, part_bytes;
+};
+
+// Chunk length (a multiple of 64 tokens) so that about 512 workgroups cover the context,
+// bounded by what the scores and the per-wave sums take in LDS.
+AttnPlan attn_plan(const attn_gqa_desc_t* d, int B, int max_len, bool unpacked) {
+  AttnPlan p{};
+  const int G = d->num_q_heads / d->num_kv_heads;
+  p.hpw = unpacked ? 1 : G;
+  const int D = d->head_dim;
+  const int fixed = 4 * p.hpw * D * 4 + 2 * p.hpw * 4;
+  int cmax = (kAttnLdsMax - fixed) / (p.hpw * 4);
+  cmax = cmax / 64 * 64;
+  if (cmax > 1024) cmax = 1024;
+  const int wg_per_chunk = B * (d->num_q_heads / p.hpw);
+  const int want = (512 + wg_per_chunk - 1) / wg_per_chunk;   // chunks per sequence
+  int c = (max_len + want - 1) / want;
+  c = (c + 63) / 64 * 64;
+  if (c < 64) c = 64;
+  if (c > cmax) c = cmax;
+  p.chunk = c;
+  p.nchunks = max_len > 0 ? (max_len + c - 1) / c : 1;
+  p.lds = (size_t)p.hpw * c * 4 + fixed;
+  p.part_bytes = (size_t)B * d->num_q_heads * p.nchunks * (D + 4) * 4;
+  return p;
+}
+
+int ilog2(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+}  // namespace
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t attn_gqa_decode_workspace_bytes(const attn_gqa_desc_t* desc, int32_t batch,
+                                                  int32_t max_seq_len) {
+  if (!attn_desc_ok(desc) || batch < 0 || max_seq_len < 0) return 0;
+  const AttnPlan p1 = attn_plan(desc, batch, max_seq_len, false);
+  const AttnPlan p2 = attn_plan(desc, batch, max_seq_len, true);
+  const size_t b = p1.part_bytes > p2.part_bytes ? p1.part_bytes : p2.part_bytes;
+  return ((b > 0 ? b : 16) + 255) / 256 * 256;
+}
+
+extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
+                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                               int32_t max_seq_len, float* out, int32_t flags, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (!desc) return MOE_INVALID_ARG;
+  if (!attn_desc_ok(desc)) return MOE_UNSUPPORTED;
+  if (batch < 0 || max_seq_len < 0 || (flags & ~ATTN_FLAG_UNPACKED)) return MOE_INVALID_ARG;
+  if (batch == 0) return MOE_OK;
+  if (!q || !out || !seq_lens || ((uintptr_t)q & 15) || ((uintptr_t)out & 15)) return MOE_INVALID_ARG;
+  if (max_seq_len > 0) {
+    if (!k_cache || !v_cache || !block_table || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+        ((uintptr_t)k_cache & 15) || ((uintptr_t)v_cache & 15))
+      return MOE_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * desc->block_size < max_seq_len) return MOE_INVALID_ARG;
+  }
+  if (!workspace || ((uintptr_t)workspace & 255)) return MOE_INVALID_ARG;
+  if (ws_bytes < attn_gqa_decode_workspace_bytes(desc, batch, max_seq_len))
+    return MOE_WORKSPACE_TOO_SMALL;
+  const bool unpacked = (flags & ATTN_FLAG_UNPACKED) != 0;
+  const AttnPlan p = attn_plan(desc, batch, max_seq_len, unpacked);
+  AttnArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.table = block_table;
+  a.lens = seq_lens;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.Hq = desc->num_q_heads;
+  a.Hkv = desc->num_kv_heads;
+  a.bs_shift = ilog2(desc->block_size);
+  a.MB = max_blocks_per_seq;
+  a.nblocks = num_blocks;
+  a.max_len = max_seq_len;
+  a.chunk = p.chunk;
+  a.nchunks = p.nchunks;
+  a.scale = desc->scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = desc->head_dim;
+  if (max_seq_len > 0) {
+    const dim3 grid(p.nchunks, desc->num_q_heads / p.hpw, batch);
+#define ATTN_SPLIT(DV, HV) \
+  hipLaunchKernelGGL((k_attn_split<DV, HV>), grid, dim3(kAttnThreads), p.lds, s, a)
+#define ATTN_SPLIT_D(HV)              \
+  do {                                \
+    if (D == 64) ATTN_SPLIT(64, HV);  \
+    else if (D == 128) ATTN_SPLIT(128, HV); \
+    else ATTN_SPLIT(256, HV);         \
+  } while (0)
+    switch (p.hpw) {
+      case 1: ATTN_SPLIT_D(1); break;
+      case 2: ATTN_SPLIT_D(2); break;
+      case 4: ATTN_SPLIT_D(4); break;
+      default: ATTN_SPLIT_D(8); break;
+    }
+#undef ATTN_SPLIT_D
+#undef ATTN_SPLIT
+    if (hipGetLastError() != hipSuccess) return MOE_HIP_ERROR;
+  }
+  const dim3 gridc(desc->num_q_heads, batch);
+  if (D == 64) hipLaunchKernelGGL((k_attn_combine<64>), gridc, dim3(64), 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((k_attn_combine<128>), gridc, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_combine<256>), gridc, dim3(64), 0, s, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}

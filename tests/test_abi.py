@@ -20,6 +20,49 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
 
 
+ATTN_HEADER = os.path.join(ROOT, "include", "attn_gqa.h")
+
+
+def declared_in(path):
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**((?:moe|attn|delta)_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_every_header_is_exported():
+    """Each header's declarations are exactly its binding's export list, and the library
+    exports every one of them."""
+    from bit_grouped_gemm_amd import attn_gqa
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for path, exports in ((HEADER, M.EXPORTS), (ATTN_HEADER, attn_gqa.EXPORTS)):
+        names = declared_in(path)
+        assert set(names) == set(exports), path
+        for n in names:
+            assert hasattr(lib, n), n
+
+
+def test_attention_rejections():
+    from bit_grouped_gemm_amd import attn_gqa as G
+    L = G._lib()
+    ok = G.desc(16, 2, 128, 64)
+    assert G.workspace_bytes(ok, 1, 32768) >= 16 * 128 * 4
+    for bad in (G.desc(16, 2, 96, 64), G.desc(16, 3, 128, 64), G.desc(32, 2, 128, 64),
+                G.desc(16, 2, 128, 48)):
+        assert G.workspace_bytes(bad, 1, 100) == 0
+        assert L.attn_gqa_decode(ctypes.byref(bad), FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 1, 100,
+                                 FAKE, 0, FAKE, 1 << 30, None) == M.MOE_UNSUPPORTED
+    # the block table cannot hold max_seq_len tokens; a bad flag; a workspace too small
+    assert L.attn_gqa_decode(ctypes.byref(ok), FAKE, FAKE, FAKE, 4, FAKE, 1, FAKE, 1, 65, FAKE, 0,
+                             FAKE, 1 << 30, None) == M.MOE_INVALID_ARG
+    assert L.attn_gqa_decode(ctypes.byref(ok), FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, 1, 65, FAKE, 2,
+                             FAKE, 1 << 30, None) == M.MOE_INVALID_ARG
+    assert L.attn_gqa_decode(ctypes.byref(ok), FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, 1, 65, FAKE, 0,
+                             FAKE, 16, None) == M.MOE_WORKSPACE_TOO_SMALL
+    assert L.attn_gqa_decode(ctypes.byref(ok), None, None, None, 0, None, 0, None, 0, 0, None, 0,
+                             None, 0, None) == M.MOE_OK
+
+
 def test_header_declares_the_five_layer_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm_w4", "moe_combine", "moe_layer_forward"):
