@@ -31,7 +31,7 @@ class DeltaShape:
 # the model's linear-attention layers: hidden 2048 as 16 heads of 128 (the plainest reading of
 # the pages, which give the layer type and its fixed-size state but no head geometry)
 DELTA_SHAPES = {
-    "tiny": DeltaShape(2, 4, 16, 32),
+    "tiny": DeltaShape(2, 4, 64, 16),
     "mid": DeltaShape(4, 4, 64, 64),
     "full": DeltaShape(16, 16, 128, 128),
     "gva": DeltaShape(8, 16, 128, 128),

@@ -21,6 +21,7 @@ def declared_functions():
 
 
 ATTN_HEADER = os.path.join(ROOT, "include", "attn_gqa.h")
+DELTA_HEADER = os.path.join(ROOT, "include", "delta_rule.h")
 
 
 def declared_in(path):
@@ -33,9 +34,10 @@ def declared_in(path):
 def test_every_header_is_exported():
     """Each header's declarations are exactly its binding's export list, and the library
     exports every one of them."""
-    from bit_grouped_gemm_amd import attn_gqa
+    from bit_grouped_gemm_amd import attn_gqa, delta_rule
     lib = ctypes.CDLL(M.LIB_PATH)
-    for path, exports in ((HEADER, M.EXPORTS), (ATTN_HEADER, attn_gqa.EXPORTS)):
+    for path, exports in ((HEADER, M.EXPORTS), (ATTN_HEADER, attn_gqa.EXPORTS),
+                          (DELTA_HEADER, delta_rule.EXPORTS)):
         names = declared_in(path)
         assert set(names) == set(exports), path
         for n in names:
@@ -61,6 +63,21 @@ def test_attention_rejections():
                              FAKE, 16, None) == M.MOE_WORKSPACE_TOO_SMALL
     assert L.attn_gqa_decode(ctypes.byref(ok), None, None, None, 0, None, 0, None, 0, 0, None, 0,
                              None, 0, None) == M.MOE_OK
+
+
+def test_delta_rule_rejections():
+    from bit_grouped_gemm_amd import delta_rule as DR
+    L = DR._lib()
+    call = lambda d, B=1, T=1, sin=FAKE: L.delta_rule_forward(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, sin, FAKE, FAKE, B, T, None)
+    for bad in (DR.desc(16, 16, 96, 128), DR.desc(16, 24, 128, 128), DR.desc(16, 16, 128, 120)):
+        assert call(bad) == M.MOE_UNSUPPORTED
+    ok = DR.desc(16, 16, 128, 128)
+    assert call(ok, T=-1) == M.MOE_INVALID_ARG
+    assert call(ok, B=0) == M.MOE_OK
+    assert call(DR.desc(16, 16, 128, 128, eps=-1.0)) == M.MOE_INVALID_ARG
+    assert L.delta_rule_forward(ctypes.byref(ok), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 1, 1, None) == M.MOE_INVALID_ARG   # misaligned q
 
 
 def test_header_declares_the_five_layer_calls():
