@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle CPU-baseline budget of the decode leg")
     ap.add_argument("--only", choices=["decode_t1", "decode_t8", "prefill_uniform",
-                                       "prefill_skewed", "stack", "copy", "peaks"])
+                                       "prefill_skewed", "stack", "copy", "peaks", "attn",
+                                       "delta"])
     ap.add_argument("--skip-cpu", action="store_true")
     return ap.parse_args()
 
@@ -407,6 +408,91 @@ def stack_section(pool: Pool):
             / 1e9 / HBM_PEAK_GBS}
 
 
+def attention_section(contexts=(4096, 32768, 131072)):
+    """GQA decode attention of the model's full-attention layers (16 query heads, 2 KV heads,
+    head size 128, 64-token cache blocks), batch 1, at several context lengths. Calls rotate
+    over disjoint sequences of one 512 MiB block pool (blocks scattered by a random
+    permutation), so every call reads its keys and values from HBM. Algorithmic bytes: the
+    sequence's keys and values once, the block-table entries, q and out."""
+    import torch
+    from bit_grouped_gemm_amd import attn_gqa as G
+    import synth
+    shape = synth.ATTN_SHAPES["full"]
+    Hq, Hkv, D, BS = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.block_size
+    d = G.desc(Hq, Hkv, D, BS)
+    blk_bytes = Hkv * BS * D * 2
+    n_phys = (512 << 20) // blk_bytes
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    kc = torch.randn((n_phys, Hkv, BS, D), generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((n_phys, Hkv, BS, D), generator=gen, device="cuda").to(torch.bfloat16)
+    perm = torch.randperm(n_phys, generator=gen, device="cuda").to(torch.int32)
+    out = {}
+    for S in contexts:
+        nb = S // BS
+        nseq = min(64, n_phys // nb)
+        tables = [perm[i * nb:(i + 1) * nb].reshape(1, nb).contiguous() for i in range(nseq)]
+        lens = torch.full((1,), S, dtype=torch.int32, device="cuda")
+        qs = [torch.randn((1, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+              for _ in range(nseq)]
+        o = torch.empty((1, Hq, D), dtype=torch.float32, device="cuda")
+        ws = G.alloc_workspace(d, 1, S)
+        res = {}
+        for flags, tag in ((0, "packed"), (G.ATTN_FLAG_UNPACKED, "unpacked")):
+            calls = [(lambda i=i, f=flags: G.decode(d, qs[i].view(torch.int16), kc.view(torch.int16),
+                                                    vc.view(torch.int16), tables[i], lens, S, o, ws, f))
+                     for i in range(nseq)]
+            st = replay_stats(calls, max(4, 256 // nseq))
+            nbytes = 2.0 * Hkv * S * D * 2 + nb * 4 + Hq * D * 2 + Hq * D * 4
+            gbs = nbytes / (st["mean"] * 1e-3) / 1e9
+            res[tag] = {"us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st),
+                        "bytes_per_call": nbytes, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        res["packing_speedup"] = res["unpacked"]["us_per_call"] / res["packed"]["us_per_call"]
+        out[f"S={S}"] = res
+        del ws
+    return {"workload": "GQA decode attention, batch 1: 16 query heads, 2 KV heads, head size 128, "
+                        "bf16 KV cache in 64-token blocks scattered over a 512 MiB pool",
+            "contexts": out}
+
+
+def delta_section():
+    """The gated delta rule of the model's linear-attention layers (16 heads, 128 x 128 fp32
+    state): a decode step at batch 1 and 8, and a 512-token prefill chunk at batch 1. Calls
+    rotate over states in a pool of at least 320 MiB. Algorithmic bytes: the state read and
+    written once, plus the tokens' q, k, v, g, beta and o."""
+    import torch
+    from bit_grouped_gemm_amd import delta_rule as DR
+    import synth
+    sh = synth.DELTA_SHAPES["full"]
+    Hk, Hv, dk, dv = sh.num_k_heads, sh.num_v_heads, sh.dk, sh.dv
+    d = DR.desc(Hk, Hv, dk, dv)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    res = {}
+    for B, T in ((1, 1), (8, 1), (1, 512)):
+        state_bytes = B * Hv * dv * dk * 4
+        npool = max(4, min(320, (320 << 20) // state_bytes))
+        pool = [torch.randn((B, Hv, dv, dk), generator=gen, device="cuda") * 0.1 for _ in range(npool)]
+        q = torch.randn((B, T, Hk, dk), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        k = torch.randn((B, T, Hk, dk), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        v = torch.randn((B, T, Hv, dv), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        g = torch.log(torch.rand((B, T, Hv), generator=gen, device="cuda") * 0.099 + 0.9)
+        beta = torch.sigmoid(torch.randn((B, T, Hv), generator=gen, device="cuda"))
+        o = torch.empty((B, T, Hv, dv), device="cuda")
+        calls = [(lambda st=st: DR.forward(d, q, k, v, g, beta, st, st, o)) for st in pool]
+        n = min(len(calls), 320 if T == 1 else 16)
+        st = replay_stats(calls[:n], max(2, 640 // n) if T == 1 else 3)
+        nbytes = 2.0 * state_bytes + B * T * (2 * Hk * dk * 2 + Hv * dv * 2 + 2 * Hv * 4 + Hv * dv * 4)
+        gbs = nbytes / (st["mean"] * 1e-3) / 1e9
+        res[f"B={B},T={T}"] = {"us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st),
+                               "tokens_per_s": B * T / (st["mean"] * 1e-3),
+                               "bytes_per_call": nbytes, "achieved_gbs": gbs,
+                               "hbm_frac": gbs / HBM_PEAK_GBS}
+        del pool
+    return {"workload": "gated delta rule, 16 heads, 128 x 128 fp32 state per head; decode steps "
+                        "(T=1) and a 512-token chunk", "cases": res}
+
+
 def copy_section():
     """Calibration kernels for FETCH_SIZE / WRITE_SIZE: a plain 256 MiB device-to-device copy
     (reads and writes 256 MiB) and a 256 MiB fp32 sum (reads 256 MiB, writes 4 bytes)."""
@@ -535,6 +621,12 @@ def main():
     if args.only == "peaks":
         log(f"peaks: {measured_peaks()}")
         return
+    if args.only == "attn":
+        log(f"attention: {json.dumps(attention_section())}")
+        return
+    if args.only == "delta":
+        log(f"delta rule: {json.dumps(delta_section())}")
+        return
 
     pool = Pool(N_LAYERS)
     s = pool.shape
@@ -586,6 +678,14 @@ def main():
     st = stack_section(pool)
     log(f"stack ({st['layers']} layers): prefill {st['prefill_tokens_per_s']:.0f} tok/s, "
         f"decode {st['decode_tokens_per_s']:.0f} tok/s ({st['decode_ms_per_token'] * 1e3:.0f} us/token)")
+    attn = attention_section()
+    for k_, r_ in attn["contexts"].items():
+        log(f"decode attention {k_}: {r_['packed']['us_per_call']:.1f} us "
+            f"({r_['packed']['hbm_frac'] * 100:.1f} % of HBM), unpacked "
+            f"{r_['unpacked']['us_per_call']:.1f} us")
+    delta = delta_section()
+    for k_, r_ in delta["cases"].items():
+        log(f"delta rule {k_}: {r_['us_per_call']:.2f} us ({r_['hbm_frac'] * 100:.1f} % of HBM)")
     log(f"timed sections took {time.time() - t_all:.1f}s")
     cpu = None if args.skip_cpu else cpu_baseline(pool, args.cpu_seconds)
 
@@ -621,6 +721,8 @@ def main():
                       "roofline": roofline_hbm(d8["kernel"], peaks)},
         "prefill_t4096": prefill,
         "stack_40_layers": st,
+        "gqa_decode_attention": attn,
+        "gated_delta_rule": delta,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -15,8 +15,11 @@
 //    the block table is read per token, so chunks may span blocks of any placement. Scores of
 //    the chunk go to LDS, then each head's maximum and exponentials (fp32), then P.V with each
 //    lane accumulating 8 dimensions of G heads; the chunk's (max, sum, acc) per head is stored.
-//  * k_attn_combine: per (sequence, query head), the chunks' results are merged in chunk order
-//    (rescaled by exp(max_c - max)), so the output does not depend on scheduling.
+//    A chunk is sized so that every lane requests all its key and value rows of the chunk at
+//    once: one memory round trip per workgroup.
+//  * k_attn_combine: per (sequence, query head), the chunks' results are merged (rescaled by
+//    exp(max_c - max)) by four waves over interleaved chunks, whose sums are then added in
+//    wave order, so the output does not depend on scheduling.
 #include <cmath>
 
 #include "attn_gqa.h"
@@ -27,7 +30,6 @@ namespace moe {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kAttnLdsMax = 64 * 1024;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -61,32 +63,35 @@ __device__ __forceinline__ float group_sum(float v) {
 
 }  // namespace
 
+// Tokens of one chunk: U wave-instruction steps of the workgroup, so that each lane requests all
+// of its key and value rows of the chunk at once (one memory round trip per workgroup).
+template <int D>
+__host__ __device__ constexpr int attn_chunk() {
+  return 8 * 4 * (64 / (D / 8));   // U = 8 steps of 4 waves x (64 / (D/8)) tokens
+}
+
 // HPW query heads per workgroup (G when packed, 1 when not); D head size.
 template <int D, int HPW>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   constexpr int LPT = D / 8;     // lanes per token row (16 bytes each)
   constexpr int TPI = 64 / LPT;  // tokens per wave instruction
   constexpr int TPB = 4 * TPI;   // tokens per workgroup step
-  constexpr int U = 4;           // steps whose rows are requested before the first is used
-  extern __shared__ __attribute__((aligned(16))) float sm[];
+  constexpr int C = attn_chunk<D>();
+  constexpr int U = C / TPB;     // steps: every row of the chunk requested up front
+  __shared__ __attribute__((aligned(16))) float sc[HPW * C];       // scores, then probabilities
+  __shared__ __attribute__((aligned(16))) float wacc[4 * HPW * D];  // per-wave sums
+  __shared__ float ml[2 * HPW];                                     // max and sum per head
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int C = a.chunk, c0 = blockIdx.x * C, b = blockIdx.z;
+  const int c0 = blockIdx.x * C, b = blockIdx.z;
   const int h0 = blockIdx.y * HPW;           // first query head of the workgroup
   const int g = h0 / (a.Hq / a.Hkv);         // its KV head
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int n = min(C, len - c0);            // tokens of this chunk
   if (n <= 0) return;                        // past the sequence: the merge reads no record here
-  float* sc = sm;                            // scores, then probabilities [HPW][C]
-  float* wacc = sm + HPW * C;                // per-wave sums [4][HPW][D]
-  float* ml = wacc + 4 * HPW * D;            // [2][HPW] max and sum
 
   const int dsl = lane % LPT, tsub = lane / LPT;
-  uint4 qv[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-    qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
   const int32_t* trow = a.table + (size_t)b * a.MB;
   const int bs_mask = (1 << a.bs_shift) - 1;
   // this lane's 16 bytes of token s of the chunk (s < n)
@@ -97,33 +102,41 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     return reinterpret_cast<const uint4*>(
         cache + ((((size_t)blk * a.Hkv + g) << a.bs_shift) + (j & bs_mask)) * D + dsl * 8);
   };
+  // every key and value row of the chunk requested before the first is used
+  uint4 kv[U], vv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = u * TPB + wave * TPI + tsub;
+    kv[u] = *row(a.kc, s < n ? s : n - 1);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = u * TPB + wave * TPI + tsub;
+    vv[u] = *row(a.vc, s < n ? s : n - 1);
+  }
+  uint4 qv[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
 
   // ---- scores: q_h . k_j for the chunk's tokens, scaled
-  for (int s0 = 0; s0 < n; s0 += U * TPB) {
-    uint4 kv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * TPB + wave * TPI + tsub;
-      kv[u] = *row(a.kc, s < n ? s : n - 1);
+  for (int u = 0; u < U; ++u) {
+    const int s = u * TPB + wave * TPI + tsub;
+    float t[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
+      d = dot2_bf16(kv[u].y, qv[hh].y, d);
+      d = dot2_bf16(kv[u].z, qv[hh].z, d);
+      d = dot2_bf16(kv[u].w, qv[hh].w, d);
+      t[hh] = group_sum<LPT>(d);
     }
+    float val = 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * TPB + wave * TPI + tsub;
-      float t[HPW];
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
-        d = dot2_bf16(kv[u].y, qv[hh].y, d);
-        d = dot2_bf16(kv[u].z, qv[hh].z, d);
-        d = dot2_bf16(kv[u].w, qv[hh].w, d);
-        t[hh] = group_sum<LPT>(d);
-      }
-      float val = 0.0f;
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
-        if (dsl == hh) val = t[hh];
-      if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
-    }
+    for (int hh = 0; hh < HPW; ++hh)
+      if (dsl == hh) val = t[hh];
+    if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
   }
   __syncthreads();
 
@@ -153,30 +166,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
-  for (int s0 = 0; s0 < n; s0 += U * TPB) {
-    uint4 vv[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * TPB + wave * TPI + tsub;
-      vv[u] = *row(a.vc, s < n ? s : n - 1);
-    }
+  for (int u = 0; u < U; ++u) {
+    const int s = u * TPB + wave * TPI + tsub;
+    if (s < n) {
+      const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      float v8[8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * TPB + wave * TPI + tsub;
-      if (s < n) {
-        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-        float v8[8];
+      for (int e = 0; e < 4; ++e) {
+        v8[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+        v8[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v8[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-          v8[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-        }
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float p = sc[hh * C + s];
 #pragma unroll
-        for (int hh = 0; hh < HPW; ++hh) {
-          const float p = sc[hh * C + s];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, v8[e], acc[hh][e]);
-        }
+        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, v8[e], acc[hh][e]);
       }
     }
   }
@@ -208,35 +213,51 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   }
 }
 
-// One wave per (query head, sequence): the chunks' records merged in chunk order.
+// One workgroup of 4 waves per (query head, sequence): the chunks' records merged. Wave w sums
+// chunks w, w + 4, ... (lanes over the dimensions), then the four waves' sums are added in wave
+// order, so the result does not depend on scheduling.
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  __shared__ float red[4];
+  __shared__ float wsum[4][D + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int nc = (len + a.chunk - 1) / a.chunk;
   float* o = a.out + ((size_t)b * a.Hq + h) * D;
   if (nc == 0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[lane + 64 * i] = 0.0f;
+    for (int i = tid; i < D; i += kAttnThreads) o[i] = 0.0f;
     return;
   }
   const size_t rec = (size_t)(D + 4);
   const float* r = a.part + ((size_t)b * a.Hq + h) * a.nchunks * rec;
+  // the maximum over the chunks
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, r[c * rec]);
+  for (int c = tid; c < nc; c += kAttnThreads) M = fmaxf(M, r[c * rec]);
+  M = wave_max_f(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float L = 0.0f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  for (int c = 0; c < nc; ++c) {
+  for (int c = wave; c < nc; c += 4) {
     const float w = __expf(r[c * rec] - M);
     L = __builtin_fmaf(w, r[c * rec + 1], L);
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, r[c * rec + 4 + lane + 64 * i], acc[i]);
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[lane + 64 * i] = acc[i] / L;
+  for (int i = 0; i < PER; ++i) wsum[wave][lane + 64 * i] = acc[i];
+  if (lane == 0) wsum[wave][D] = L;
+  __syncthreads();
+  if (tid < D) {
+    const float tot = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+    const float ltot = ((wsum[0][D] + wsum[1][D]) + wsum[2][D]) + wsum[3][D];
+    o[tid] = tot / ltot;
+  }
 }
 
 // ------------------------------------------------------------------------------ host side
@@ -257,26 +278,16 @@ struct AttnPlan {
   size_t lds, part_bytes;
 };
 
-// Chunk length (a multiple of 64 tokens) so that about 512 workgroups cover the context,
-// bounded by what the scores and the per-wave sums take in LDS.
+// The chunk length is fixed per head size (attn_chunk<D>(): 256, 128 or 64 tokens for D = 64,
+// 128, 256), so that each lane requests all of its rows of a chunk at once.
 AttnPlan attn_plan(const attn_gqa_desc_t* d, int B, int max_len, bool unpacked) {
   AttnPlan p{};
   const int G = d->num_q_heads / d->num_kv_heads;
   p.hpw = unpacked ? 1 : G;
   const int D = d->head_dim;
-  const int fixed = 4 * p.hpw * D * 4 + 2 * p.hpw * 4;
-  int cmax = (kAttnLdsMax - fixed) / (p.hpw * 4);
-  cmax = cmax / 64 * 64;
-  if (cmax > 1024) cmax = 1024;
-  const int wg_per_chunk = B * (d->num_q_heads / p.hpw);
-  const int want = (512 + wg_per_chunk - 1) / wg_per_chunk;   // chunks per sequence
-  int c = (max_len + want - 1) / want;
-  c = (c + 63) / 64 * 64;
-  if (c < 64) c = 64;
-  if (c > cmax) c = cmax;
-  p.chunk = c;
-  p.nchunks = max_len > 0 ? (max_len + c - 1) / c : 1;
-  p.lds = (size_t)p.hpw * c * 4 + fixed;
+  p.chunk = D == 64 ? attn_chunk<64>() : D == 128 ? attn_chunk<128>() : attn_chunk<256>();
+  p.nchunks = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 1;
+  p.lds = 0;
   p.part_bytes = (size_t)B * d->num_q_heads * p.nchunks * (D + 4) * 4;
   return p;
 }
@@ -346,7 +357,7 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
   if (max_seq_len > 0) {
     const dim3 grid(p.nchunks, desc->num_q_heads / p.hpw, batch);
 #define ATTN_SPLIT(DV, HV) \
-  hipLaunchKernelGGL((k_attn_split<DV, HV>), grid, dim3(kAttnThreads), p.lds, s, a)
+  hipLaunchKernelGGL((k_attn_split<DV, HV>), grid, dim3(kAttnThreads), 0, s, a)
 #define ATTN_SPLIT_D(HV)              \
   do {                                \
     if (D == 64) ATTN_SPLIT(64, HV);  \
@@ -364,8 +375,8 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
     if (hipGetLastError() != hipSuccess) return MOE_HIP_ERROR;
   }
   const dim3 gridc(desc->num_q_heads, batch);
-  if (D == 64) hipLaunchKernelGGL((k_attn_combine<64>), gridc, dim3(64), 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((k_attn_combine<128>), gridc, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_combine<256>), gridc, dim3(64), 0, s, a);
+  if (D == 64) hipLaunchKernelGGL((k_attn_combine<64>), gridc, dim3(kAttnThreads), 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((k_attn_combine<128>), gridc, dim3(kAttnThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_combine<256>), gridc, dim3(kAttnThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
