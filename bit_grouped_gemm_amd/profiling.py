@@ -5,10 +5,13 @@ HBM traffic per launch from the FETCH_SIZE / WRITE_SIZE counters.
     python -m bit_grouped_gemm_amd.profiling traffic --fetch DIR --write DIR \
         --copy-fetch DIR --copy-write DIR --copy-bytes N --kernel REGEX --key NAME \
         --out profiles/traffic.json
+    python -m bit_grouped_gemm_amd.profiling counters PMC_DIR --cmd "COMMAND" --out FILE.md
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch. They count what the L2 requests
 from the memory fabric, so each is divided by the ratio it shows on a plain device copy of a
-known size (the copy-calibration runs) before it is taken as HBM bytes.
+known size (the copy-calibration runs) before it is taken as HBM bytes. The same calibration
+run also holds a read-only reduction over the same bytes; its FETCH_SIZE ratio is stored beside
+the copy's as a cross-check of the factor.
 """
 from __future__ import annotations
 
@@ -109,6 +112,10 @@ def copy_factor(pmc_dir: str, counter: str, nbytes: int, kernel_regex: str = "co
 def update_traffic(args):
     ff, nf = copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes)
     fw, nw = copy_factor(args.copy_write, "WRITE_SIZE", args.copy_bytes)
+    try:   # the read-only reduction of the calibration run (absent in older runs)
+        fr, _ = copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes, "reduce")
+    except ValueError:
+        fr = None
     fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
     write = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel)
     data = {}
@@ -118,7 +125,7 @@ def update_traffic(args):
     if data.get("source_hash") != h:
         data = {"source_hash": h, "kernels": {}}
     data["copy_calibration"] = {"bytes": args.copy_bytes, "fetch_factor": ff, "write_factor": fw,
-                                "dispatches": [nf, nw]}
+                                "dispatches": [nf, nw], "read_only_fetch_factor": fr}
     fk, wk = statistics.fmean(fetch), statistics.fmean(write)
     data["kernels"][args.key] = {
         "kernel_regex": args.kernel, "dispatches": [len(fetch), len(write)],
@@ -128,6 +135,33 @@ def update_traffic(args):
     with open(args.out, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(data["kernels"][args.key]))
+
+
+def counter_table(pmc_dir: str):
+    """Mean value per dispatch of every counter, per kernel (short name): {kernel: {counter: (n, mean)}}."""
+    agg: "OrderedDict[str, dict]" = OrderedDict()
+    for r in csv.DictReader(open(_find(pmc_dir, "_counter_collection.csv"))):
+        k = short_name(r["Kernel_Name"])
+        agg.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return OrderedDict((k, {c: (len(v), statistics.fmean(v)) for c, v in cs.items()})
+                       for k, cs in agg.items())
+
+
+def write_counters_md(pmc_dir: str, cmd: str, out: str, title: str, top: int = 20):
+    tab = counter_table(pmc_dir)
+    names = sorted({c for cs in tab.values() for c in cs})
+    lines = [f"# {title}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
+             "Mean per dispatch (counters summed over the chip).", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---:|" + "---:|" * len(names)]
+    rows = sorted(tab.items(), key=lambda kv: -max(v[1] for v in kv[1].values()))[:top]
+    for k, cs in rows:
+        n = max(v[0] for v in cs.values())
+        vals = " | ".join(f"{cs[c][1]:.3g}" if c in cs else "" for c in names)
+        lines.append(f"| `{k}` | {n} | {vals} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return tab
 
 
 def main():
@@ -142,7 +176,16 @@ def main():
     for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "key", "out"):
         t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
     t.add_argument("--copy-bytes", dest="copy_bytes", type=int, default=256 << 20)
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dir")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--title", default="rocprofv3 counters")
     args = ap.parse_args()
+    if args.action == "counters":
+        for k, cs in list(write_counters_md(args.pmc_dir, args.cmd, args.out, args.title).items())[:12]:
+            print(k[:60], {c: round(v[1], 1) for c, v in cs.items()})
+        return
     if args.action == "stats":
         for r in write_stats_md(args.trace_dir, args.cmd, args.out, args.title)[:12]:
             print(f"{r['kernel'][:60]:60s} {r['calls']:6d} {r['avg_us']:9.2f}")
