@@ -289,8 +289,7 @@ def moe_bench_stream_read(buf, workgroups: int, sink, stream=None):
     """Enqueue the streaming-read measurement kernel over the whole of buf."""
     nbytes = buf.numel() * buf.element_size()
     _check(lib().moe_bench_stream_read(_p(buf), nbytes, workgroups, _p(sink), _stream(stream)),
-           "moe_bench_stream_read", "moe_layer_forward_noalloc")
-NOALLOC_SCRATCH_BYTES = 64 << 20
+           "moe_bench_stream_read")
 
 
 def moe_layer_num_phases(layer, T: int, flags: int = 0) -> int:
