@@ -9,17 +9,22 @@
 // the work is plain fp32 VALU arithmetic (dot2 on bf16 pairs), not MFMA.
 //
 // Layout of the work (split over the context, then a merge):
-//  * k_attn_split: one workgroup of 4 waves per (sequence, KV head, chunk of the context) with
-//    all G query heads of that KV head (packed). A token's key row of D bf16 is read by D/8
-//    consecutive lanes, 16 bytes each, so one wave instruction reads whole rows (64 * 16 bytes);
-//    the block table is read per token, so chunks may span blocks of any placement. Scores of
-//    the chunk go to LDS, then each head's maximum and exponentials (fp32), then P.V with each
-//    lane accumulating 8 dimensions of G heads; the chunk's (max, sum, acc) per head is stored.
-//    A chunk is sized so that every lane requests all its key and value rows of the chunk at
-//    once: one memory round trip per workgroup.
-//  * k_attn_combine: per (sequence, query head), the chunks' results are merged (rescaled by
-//    exp(max_c - max)) by four waves over interleaved chunks, whose sums are then added in
-//    wave order, so the output does not depend on scheduling.
+//  * k_attn_split: one workgroup of 4 waves per (sequence, KV head, span of the context) with
+//    all G query heads of that KV head (packed). A span is a run of chunks; a token's key row of
+//    D bf16 is read by D/8 consecutive lanes, 16 bytes each, so one wave instruction reads whole
+//    rows (64 * 16 bytes); the block table is read per token, so chunks may span blocks of any
+//    placement. Per chunk: scores to LDS, each head's running maximum and the chunk's
+//    exponentials (fp32, online softmax: earlier sums are rescaled by exp(m_old - m_new)), then
+//    P.V with each lane accumulating 8 dimensions of G heads. A chunk is sized so that every
+//    lane requests all its key and value rows of the chunk at once, and the next chunk's keys
+//    (values) are requested as soon as the current ones have been used, so a workgroup keeps a
+//    chunk's rows in flight while it computes. The span's (max, sum, acc) per head is stored.
+//    The spans are sized so that a set number of workgroups covers the call.
+//  * k_attn_combine: per (sequence, query head), the spans' records are merged, rescaled by
+//    exp(max_s - max): weights first, then D/4 lanes per record with 16-byte loads over
+//    interleaved records, summed over the lanes' partial sums in a fixed order, so the output
+//    does not depend on scheduling.
+#include <algorithm>
 #include <cmath>
 
 #include "attn_gqa.h"
@@ -31,15 +36,23 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 
+// Split workgroups a call is spread over: 512 with packed heads (a packed workgroup does G
+// heads' arithmetic per byte and already keeps the chip busy), 1024 with one head per workgroup.
+constexpr int kAttnTargetWorkgroups = 512;
+constexpr int kAttnTargetWorkgroupsUnpacked = 1024;
+constexpr int kAttnMaxSpans = 1024;  // spans per (sequence, head): bounds the merge's LDS
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kc;
   const uint16_t* vc;
   const int32_t* table;
   const int32_t* lens;
-  float* part;  // [B, Hq, nchunks, D + 4]: max, sum, -, -, acc[D]
+  float* part;  // [B, Hq, nspans, D + 4]: max, sum, -, -, acc[D]
   float* out;   // [B, Hq, D]
-  int Hq, Hkv, bs_shift, MB, nblocks, max_len, chunk, nchunks;
+  int Hq, Hkv, bs_shift, MB, nblocks, max_len;
+  int span;     // tokens per span: a multiple of the chunk
+  int nspans;   // spans of the longest sequence (the record stride)
   float scale;
 };
 
@@ -64,127 +77,149 @@ __device__ __forceinline__ float group_sum(float v) {
 }  // namespace
 
 // Tokens of one chunk: U wave-instruction steps of the workgroup, so that each lane requests all
-// of its key and value rows of the chunk at once (one memory round trip per workgroup).
-template <int D>
+// of its key and value rows of the chunk at once (one memory round trip per chunk). U = 8 for
+// long contexts; U = 2 (chunks a quarter as long) when the long chunks would leave the grid
+// short of workgroups.
+template <int D, int U>
 __host__ __device__ constexpr int attn_chunk() {
-  return 8 * 4 * (64 / (D / 8));   // U = 8 steps of 4 waves x (64 / (D/8)) tokens
+  return U * 4 * (64 / (D / 8));   // U steps of 4 waves x (64 / (D/8)) tokens
 }
 
-// HPW query heads per workgroup (G when packed, 1 when not); D head size.
-template <int D, int HPW>
+// HPW query heads per workgroup (G when packed, 1 when not); D head size; U steps per chunk.
+template <int D, int HPW, int U>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   constexpr int LPT = D / 8;     // lanes per token row (16 bytes each)
   constexpr int TPI = 64 / LPT;  // tokens per wave instruction
   constexpr int TPB = 4 * TPI;   // tokens per workgroup step
-  constexpr int C = attn_chunk<D>();
-  constexpr int U = C / TPB;     // steps: every row of the chunk requested up front
+  constexpr int C = attn_chunk<D, U>();  // U steps: every row of a chunk requested up front
   __shared__ __attribute__((aligned(16))) float sc[HPW * C];       // scores, then probabilities
   __shared__ __attribute__((aligned(16))) float wacc[4 * HPW * D];  // per-wave sums
-  __shared__ float ml[2 * HPW];                                     // max and sum per head
+  __shared__ float st[3 * HPW];   // per head: running max, running sum, this chunk's rescale
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = blockIdx.x * C, b = blockIdx.z;
+  const int b = blockIdx.z;
   const int h0 = blockIdx.y * HPW;           // first query head of the workgroup
   const int g = h0 / (a.Hq / a.Hkv);         // its KV head
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int n = min(C, len - c0);            // tokens of this chunk
-  if (n <= 0) return;                        // past the sequence: the merge reads no record here
+  const int t0 = blockIdx.x * a.span;
+  const int t1 = min(len, t0 + a.span);      // this span: tokens [t0, t1)
+  if (t1 <= t0) return;                      // past the sequence: the merge reads no record here
 
   const int dsl = lane % LPT, tsub = lane / LPT;
   const int32_t* trow = a.table + (size_t)b * a.MB;
   const int bs_mask = (1 << a.bs_shift) - 1;
-  // this lane's 16 bytes of token s of the chunk (s < n)
-  auto row = [&](const uint16_t* cache, int s) -> const uint4* {
-    const int j = c0 + s;
+  // this lane's 16 bytes of token j (j < t1)
+  auto row = [&](const uint16_t* cache, int j) -> const uint4* {
     int blk = trow[j >> a.bs_shift];
     blk = blk < 0 ? 0 : (blk >= a.nblocks ? a.nblocks - 1 : blk);
     return reinterpret_cast<const uint4*>(
         cache + ((((size_t)blk * a.Hkv + g) << a.bs_shift) + (j & bs_mask)) * D + dsl * 8);
   };
-  // every key and value row of the chunk requested before the first is used
+  // token of step u of the chunk at c0, clamped into the span (the clamped rows are not used)
+  auto tok = [&](int c0, int u) { return min(c0 + u * TPB + wave * TPI + tsub, t1 - 1); };
   uint4 kv[U], vv[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = u * TPB + wave * TPI + tsub;
-    kv[u] = *row(a.kc, s < n ? s : n - 1);
-  }
+  for (int u = 0; u < U; ++u) kv[u] = *row(a.kc, tok(t0, u));
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = u * TPB + wave * TPI + tsub;
-    vv[u] = *row(a.vc, s < n ? s : n - 1);
-  }
+  for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(t0, u));
   uint4 qv[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
     qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
-
-  // ---- scores: q_h . k_j for the chunk's tokens, scaled
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = u * TPB + wave * TPI + tsub;
-    float t[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
-      d = dot2_bf16(kv[u].y, qv[hh].y, d);
-      d = dot2_bf16(kv[u].z, qv[hh].z, d);
-      d = dot2_bf16(kv[u].w, qv[hh].w, d);
-      t[hh] = group_sum<LPT>(d);
-    }
-    float val = 0.0f;
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh)
-      if (dsl == hh) val = t[hh];
-    if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
+  if (tid < HPW) {
+    st[tid] = -INFINITY;
+    st[HPW + tid] = 0.0f;
   }
-  __syncthreads();
-
-  // ---- per head: maximum, exponentials (kept in place) and their sum
-  for (int hh = wave; hh < HPW; hh += 4) {
-    float* sh = sc + hh * C;
-    float m = -INFINITY;
-    for (int i = lane; i < n; i += 64) m = fmaxf(m, sh[i]);
-    m = wave_max_f(m);
-    float l = 0.0f;
-    for (int i = lane; i < n; i += 64) {
-      const float p = __expf(sh[i] - m);
-      sh[i] = p;
-      l += p;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      ml[hh] = m;
-      ml[HPW + hh] = l;
-    }
-  }
-  __syncthreads();
-
-  // ---- P.V: each lane accumulates its 8 dimensions for the HPW heads
   float acc[HPW][8];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+
+  for (int c0 = t0; c0 < t1; c0 += C) {
+    const int n = min(C, t1 - c0);           // tokens of this chunk
+    const bool more = c0 + C < t1;
+    // ---- scores: q_h . k_j for the chunk's tokens, scaled
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = u * TPB + wave * TPI + tsub;
-    if (s < n) {
-      const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-      float v8[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v8[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-        v8[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int s = u * TPB + wave * TPI + tsub;
+      float t[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        const float p = sc[hh * C + s];
+        float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
+        d = dot2_bf16(kv[u].y, qv[hh].y, d);
+        d = dot2_bf16(kv[u].z, qv[hh].z, d);
+        d = dot2_bf16(kv[u].w, qv[hh].w, d);
+        t[hh] = group_sum<LPT>(d);
+      }
+      float val = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, v8[e], acc[hh][e]);
+      for (int hh = 0; hh < HPW; ++hh)
+        if (dsl == hh) val = t[hh];
+      if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
+    }
+    if (more) {   // the keys are used: request the next chunk's
+#pragma unroll
+      for (int u = 0; u < U; ++u) kv[u] = *row(a.kc, tok(c0 + C, u));
+    }
+    __syncthreads();
+
+    // ---- per head: new running maximum, exponentials (kept in place), sums
+    for (int hh = wave; hh < HPW; hh += 4) {
+      float* sh = sc + hh * C;
+      float m = -INFINITY;
+      for (int i = lane; i < n; i += 64) m = fmaxf(m, sh[i]);
+      m = fmaxf(wave_max_f(m), st[hh]);
+      float l = 0.0f;
+      for (int i = lane; i < n; i += 64) {
+        const float p = __expf(sh[i] - m);
+        sh[i] = p;
+        l += p;
+      }
+      l = wave_sum(l);
+      if (lane == 0) {
+        const float f = __expf(st[hh] - m);  // 0 for the first chunk (old max -inf)
+        st[hh] = m;
+        st[HPW + hh] = __builtin_fmaf(st[HPW + hh], f, l);
+        st[2 * HPW + hh] = f;
       }
     }
+    __syncthreads();
+
+    // ---- P.V: each lane accumulates its 8 dimensions for the HPW heads
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const float f = st[2 * HPW + hh];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = u * TPB + wave * TPI + tsub;
+      if (s < n) {
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+          v8[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        }
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const float p = sc[hh * C + s];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] = __builtin_fmaf(p, v8[e], acc[hh][e]);
+        }
+      }
+    }
+    if (more) {   // the values are used: request the next chunk's
+#pragma unroll
+      for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(c0 + C, u));
+    }
+    __syncthreads();   // the next chunk's scores overwrite sc and st
   }
+
   // sum over the wave's token groups (lanes with the same dimensions), then over the waves
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1)
@@ -200,63 +235,89 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   }
   __syncthreads();
   const size_t rec = (size_t)(D + 4);
-  float* part = a.part + (((size_t)b * a.Hq + h0) * a.nchunks + blockIdx.x) * rec;
+  float* part = a.part + (((size_t)b * a.Hq + h0) * a.nspans + blockIdx.x) * rec;
   for (int i = tid; i < HPW * D; i += kAttnThreads) {
     const int hh = i / D, d = i % D;
     const float s = ((wacc[hh * D + d] + wacc[(HPW + hh) * D + d]) + wacc[(2 * HPW + hh) * D + d]) +
                     wacc[(3 * HPW + hh) * D + d];
-    part[hh * a.nchunks * rec + 4 + d] = s;
+    part[hh * a.nspans * rec + 4 + d] = s;
   }
   if (tid < HPW) {
-    part[tid * a.nchunks * rec + 0] = ml[tid];
-    part[tid * a.nchunks * rec + 1] = ml[HPW + tid];
+    part[tid * a.nspans * rec + 0] = st[tid];
+    part[tid * a.nspans * rec + 1] = st[HPW + tid];
   }
 }
 
-// One workgroup of 4 waves per (query head, sequence): the chunks' records merged. Wave w sums
-// chunks w, w + 4, ... (lanes over the dimensions), then the four waves' sums are added in wave
-// order, so the result does not depend on scheduling.
+// One workgroup per (query head, sequence): the spans' records merged. The weights
+// exp(max_s - max) go to LDS; then lanes take 4 dimensions of a record each (D/4 lanes per
+// record, 256 / (D/4) records per step over interleaved records) and the per-slot sums are
+// added in slot order, so the result does not depend on scheduling.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
-  constexpr int PER = D / 64;
-  __shared__ float red[4];
-  __shared__ float wsum[4][D + 1];
+  constexpr int TPR = D / 4;              // lanes per record
+  constexpr int RPS = kAttnThreads / TPR; // records per step
+  constexpr int UNR = 8;                  // records per lane requested together
+  __shared__ float wts[kAttnMaxSpans];
+  __shared__ float red[8];
+  __shared__ __attribute__((aligned(16))) float part_sum[RPS * D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int nc = (len + a.chunk - 1) / a.chunk;
+  const int ns = (len + a.span - 1) / a.span;
   float* o = a.out + ((size_t)b * a.Hq + h) * D;
-  if (nc == 0) {
+  if (ns == 0) {
     for (int i = tid; i < D; i += kAttnThreads) o[i] = 0.0f;
     return;
   }
   const size_t rec = (size_t)(D + 4);
-  const float* r = a.part + ((size_t)b * a.Hq + h) * a.nchunks * rec;
-  // the maximum over the chunks
+  const float* r = a.part + ((size_t)b * a.Hq + h) * a.nspans * rec;
+  // the maximum over the spans
   float M = -INFINITY;
-  for (int c = tid; c < nc; c += kAttnThreads) M = fmaxf(M, r[c * rec]);
+  for (int c = tid; c < ns; c += kAttnThreads) M = fmaxf(M, r[c * rec]);
   M = wave_max_f(M);
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float L = 0.0f, acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  for (int c = wave; c < nc; c += 4) {
+  // weights and the total sum
+  float L = 0.0f;
+  for (int c = tid; c < ns; c += kAttnThreads) {
     const float w = __expf(r[c * rec] - M);
+    wts[c] = w;
     L = __builtin_fmaf(w, r[c * rec + 1], L);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, r[c * rec + 4 + lane + 64 * i], acc[i]);
   }
+  L = wave_sum(L);
+  if (lane == 0) red[4 + wave] = L;
+  __syncthreads();
+  L = ((red[4] + red[5]) + red[6]) + red[7];
+  // weighted sum of the accumulators: lane slot `sl` takes records sl, sl + RPS, ...
+  const int sl = tid / TPR, d4 = (tid % TPR) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = sl; c < ns; c += UNR * RPS) {
+    float4 v[UNR];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) wsum[wave][lane + 64 * i] = acc[i];
-  if (lane == 0) wsum[wave][D] = L;
+    for (int u = 0; u < UNR; ++u) {
+      const int cc = min(c + u * RPS, ns - 1);
+      v[u] = *reinterpret_cast<const float4*>(r + cc * rec + 4 + d4);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (c + u * RPS < ns) {
+        const float w = wts[c + u * RPS];
+        acc.x = __builtin_fmaf(w, v[u].x, acc.x);
+        acc.y = __builtin_fmaf(w, v[u].y, acc.y);
+        acc.z = __builtin_fmaf(w, v[u].z, acc.z);
+        acc.w = __builtin_fmaf(w, v[u].w, acc.w);
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(part_sum + sl * D + d4) = acc;
   __syncthreads();
   if (tid < D) {
-    const float tot = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
-    const float ltot = ((wsum[0][D] + wsum[1][D]) + wsum[2][D]) + wsum[3][D];
-    o[tid] = tot / ltot;
+    float tot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < RPS; ++k) tot += part_sum[k * D + tid];
+    o[tid] = tot / L;
   }
 }
 
@@ -274,21 +335,35 @@ bool attn_desc_ok(const attn_gqa_desc_t* d) {
 }
 
 struct AttnPlan {
-  int hpw, chunk, nchunks;
-  size_t lds, part_bytes;
+  int hpw, u, chunk, span, nspans;
+  size_t part_bytes;
 };
 
-// The chunk length is fixed per head size (attn_chunk<D>(): 256, 128 or 64 tokens for D = 64,
-// 128, 256), so that each lane requests all of its rows of a chunk at once.
+int chunk_tokens(int D, int u) {
+  if (u == 8) return D == 64 ? attn_chunk<64, 8>() : D == 128 ? attn_chunk<128, 8>() : attn_chunk<256, 8>();
+  return D == 64 ? attn_chunk<64, 2>() : D == 128 ? attn_chunk<128, 2>() : attn_chunk<256, 2>();
+}
+
+// Chunks of attn_chunk<D, 8>() tokens (256, 128 or 64 for D = 64, 128, 256), or a quarter of
+// that when the long chunks would give fewer than kAttnTargetWorkgroups workgroups. Spans take as
+// many chunks as it needs to keep the grid near the target (packed or unpacked) in workgroups.
 AttnPlan attn_plan(const attn_gqa_desc_t* d, int B, int max_len, bool unpacked) {
   AttnPlan p{};
   const int G = d->num_q_heads / d->num_kv_heads;
   p.hpw = unpacked ? 1 : G;
   const int D = d->head_dim;
-  p.chunk = D == 64 ? attn_chunk<64>() : D == 128 ? attn_chunk<128>() : attn_chunk<256>();
-  p.nchunks = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 1;
-  p.lds = 0;
-  p.part_bytes = (size_t)B * d->num_q_heads * p.nchunks * (D + 4) * 4;
+  const int64_t groups = (int64_t)(B > 0 ? B : 1) * (d->num_q_heads / p.hpw);
+  const int64_t len = max_len > 0 ? max_len : 1;
+  p.u = 8;
+  if (groups * ((len + chunk_tokens(D, 8) - 1) / chunk_tokens(D, 8)) < kAttnTargetWorkgroups) p.u = 2;
+  p.chunk = chunk_tokens(D, p.u);
+  const int64_t nchunks = (len + p.chunk - 1) / p.chunk;
+  const int64_t target = p.hpw == 1 ? kAttnTargetWorkgroupsUnpacked : kAttnTargetWorkgroups;
+  const int64_t want = std::max<int64_t>(1, (target + groups - 1) / groups);
+  const int64_t cps = std::max<int64_t>(1, (nchunks + want - 1) / want);   // chunks per span
+  p.span = (int)std::min<int64_t>(cps * p.chunk, 1 << 30);
+  p.nspans = (int)((nchunks + cps - 1) / cps);
+  p.part_bytes = (size_t)(B > 0 ? B : 0) * d->num_q_heads * p.nspans * (D + 4) * 4;
   return p;
 }
 
@@ -335,6 +410,7 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
     return MOE_WORKSPACE_TOO_SMALL;
   const bool unpacked = (flags & ATTN_FLAG_UNPACKED) != 0;
   const AttnPlan p = attn_plan(desc, batch, max_seq_len, unpacked);
+  if (p.nspans > kAttnMaxSpans) return MOE_UNSUPPORTED;   // cannot happen: nspans <= target
   AttnArgs a;
   a.q = q;
   a.kc = k_cache;
@@ -349,20 +425,25 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
   a.MB = max_blocks_per_seq;
   a.nblocks = num_blocks;
   a.max_len = max_seq_len;
-  a.chunk = p.chunk;
-  a.nchunks = p.nchunks;
+  a.span = p.span;
+  a.nspans = p.nspans;
   a.scale = desc->scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = desc->head_dim;
   if (max_seq_len > 0) {
-    const dim3 grid(p.nchunks, desc->num_q_heads / p.hpw, batch);
-#define ATTN_SPLIT(DV, HV) \
-  hipLaunchKernelGGL((k_attn_split<DV, HV>), grid, dim3(kAttnThreads), 0, s, a)
-#define ATTN_SPLIT_D(HV)              \
-  do {                                \
-    if (D == 64) ATTN_SPLIT(64, HV);  \
-    else if (D == 128) ATTN_SPLIT(128, HV); \
-    else ATTN_SPLIT(256, HV);         \
+    const dim3 grid(p.nspans, desc->num_q_heads / p.hpw, batch);
+#define ATTN_SPLIT(DV, HV, UV) \
+  hipLaunchKernelGGL((k_attn_split<DV, HV, UV>), grid, dim3(kAttnThreads), 0, s, a)
+#define ATTN_SPLIT_U(DV, HV)                    \
+  do {                                          \
+    if (p.u == 8) ATTN_SPLIT(DV, HV, 8);        \
+    else ATTN_SPLIT(DV, HV, 2);                 \
+  } while (0)
+#define ATTN_SPLIT_D(HV)                        \
+  do {                                          \
+    if (D == 64) ATTN_SPLIT_U(64, HV);          \
+    else if (D == 128) ATTN_SPLIT_U(128, HV);   \
+    else ATTN_SPLIT_U(256, HV);                 \
   } while (0)
     switch (p.hpw) {
       case 1: ATTN_SPLIT_D(1); break;
@@ -371,6 +452,7 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
       default: ATTN_SPLIT_D(8); break;
     }
 #undef ATTN_SPLIT_D
+#undef ATTN_SPLIT_U
 #undef ATTN_SPLIT
     if (hipGetLastError() != hipSuccess) return MOE_HIP_ERROR;
   }

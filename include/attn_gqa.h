@@ -44,7 +44,7 @@ enum {
   ATTN_FLAG_UNPACKED = 1
 };
 
-/* Workspace for a call with these sizes (0 if the arguments are invalid): the per-chunk
+/* Workspace for a call with these sizes (0 if the arguments are invalid): the per-span
  * partial results of the split over the context. 256-byte aligned, no initialisation. */
 size_t attn_gqa_decode_workspace_bytes(const attn_gqa_desc_t* desc, int32_t batch,
                                        int32_t max_seq_len);
@@ -61,7 +61,8 @@ size_t attn_gqa_decode_workspace_bytes(const attn_gqa_desc_t* desc, int32_t batc
  * Device-side guards: lengths are clamped to max_seq_len and block ids to [0, num_blocks), so
  * that no access leaves the buffers (a wrong id gives a wrong result, not a fault).
  * flags: ATTN_FLAG_*. workspace: attn_gqa_decode_workspace_bytes(desc, B, max_seq_len).
- * Deterministic: the chunks' partial results are merged in chunk order. */
+ * Deterministic: the context is split into spans of whole chunks (sized from B, the heads and
+ * max_seq_len only) whose partial results are merged in a fixed order. */
 int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q, const uint16_t* k_cache,
                     const uint16_t* v_cache, int32_t num_blocks, const int32_t* block_table,
                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
