@@ -59,6 +59,8 @@ def parse():
                                        "prefill_skewed", "stack", "copy", "peaks", "attn",
                                        "delta"])
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--attn-contexts", default="4096,32768,131072",
+                    help="context lengths of the attention section (comma-separated)")
     return ap.parse_args()
 
 
@@ -68,17 +70,9 @@ def log(msg):
 
 def measured_traffic(key: str):
     """HBM bytes per launch from the committed counter summary (profiles/traffic.json), or None
-    if it is absent or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
-    from bit_grouped_gemm_amd.profiling import kernel_source_hash
-    if data.get("source_hash") != kernel_source_hash():
-        return None
-    entry = data.get("kernels", {}).get(key)
-    return None if entry is None else entry.get("bytes_per_launch")
+    if it is absent or was taken on other sources of that kernel."""
+    from bit_grouped_gemm_amd.profiling import traffic_entry
+    return traffic_entry(os.path.join(ROOT, "profiles", "traffic.json"), key)
 
 
 # ----------------------------------------------------------------------------- workload
@@ -447,6 +441,8 @@ def attention_section(contexts=(4096, 32768, 131072)):
             gbs = nbytes / (st["mean"] * 1e-3) / 1e9
             res[tag] = {"us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st),
                         "bytes_per_call": nbytes, "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        # HBM bytes of the packed split kernel from the committed counter runs
+        res["packed"]["split_kernel_traffic"] = measured_traffic(f"attn_split@ctx{S // 1024}k")
         res["packing_speedup"] = res["unpacked"]["us_per_call"] / res["packed"]["us_per_call"]
         out[f"S={S}"] = res
         del ws
@@ -487,7 +483,8 @@ def delta_section():
         res[f"B={B},T={T}"] = {"us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st),
                                "tokens_per_s": B * T / (st["mean"] * 1e-3),
                                "bytes_per_call": nbytes, "achieved_gbs": gbs,
-                               "hbm_frac": gbs / HBM_PEAK_GBS}
+                               "hbm_frac": gbs / HBM_PEAK_GBS,
+                               "traffic": measured_traffic(f"delta@b{B}_t{T}")}
         del pool
     return {"workload": "gated delta rule, 16 heads, 128 x 128 fp32 state per head; decode steps "
                         "(T=1) and a 512-token chunk", "cases": res}
@@ -621,8 +618,9 @@ def main():
     if args.only == "peaks":
         log(f"peaks: {measured_peaks()}")
         return
+    contexts = tuple(int(c) for c in args.attn_contexts.split(","))
     if args.only == "attn":
-        log(f"attention: {json.dumps(attention_section())}")
+        log(f"attention: {json.dumps(attention_section(contexts))}")
         return
     if args.only == "delta":
         log(f"delta rule: {json.dumps(delta_section())}")
@@ -673,12 +671,14 @@ def main():
                         "mfma_row_padding_frac": p["mfma_row_padding_frac"],
                         "phases_us": p["phases_us"],
                         "roofline": rk, "down_roofline": roofline_mfma(p["down_kernel"], peaks)}
+        prefill[tag]["down_roofline"]["traffic"] = measured_traffic(f"down@prefill_{tag}")
+        prefill[tag]["combine_traffic"] = measured_traffic(f"combine@prefill_{tag}")
         log(f"prefill T=4096 {tag}: {p['ms_per_step'] * 1e3:.1f} us/layer "
             f"({p['tokens_per_s'] / 1e6:.2f} M tok/s, {tf:.0f} TFLOP/s); phases {p['phases_us']}")
     st = stack_section(pool)
     log(f"stack ({st['layers']} layers): prefill {st['prefill_tokens_per_s']:.0f} tok/s, "
         f"decode {st['decode_tokens_per_s']:.0f} tok/s ({st['decode_ms_per_token'] * 1e3:.0f} us/token)")
-    attn = attention_section()
+    attn = attention_section(contexts)
     for k_, r_ in attn["contexts"].items():
         log(f"decode attention {k_}: {r_['packed']['us_per_call']:.1f} us "
             f"({r_['packed']['hbm_frac'] * 100:.1f} % of HBM), unpacked "

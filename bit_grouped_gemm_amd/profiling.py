@@ -3,7 +3,7 @@ HBM traffic per launch from the FETCH_SIZE / WRITE_SIZE counters.
 
     python -m bit_grouped_gemm_amd.profiling stats TRACE_DIR --cmd "COMMAND" --out FILE.md
     python -m bit_grouped_gemm_amd.profiling traffic --fetch DIR --write DIR \
-        --copy-fetch DIR --copy-write DIR --copy-bytes N --kernel REGEX --key NAME \
+        --copy-fetch DIR --copy-write DIR --copy-bytes N --kernel REGEX [--grid N] --key NAME \
         --out profiles/traffic.json
     python -m bit_grouped_gemm_amd.profiling counters PMC_DIR --cmd "COMMAND" --out FILE.md
 
@@ -28,14 +28,30 @@ from collections import OrderedDict
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; a traffic figure is valid only for the sources it was taken on."""
+def kernel_source_hash(files=None) -> str:
+    """Hash of HIP sources (all of csrc by default, else the named files of csrc); a traffic
+    figure is valid only for the sources it was taken on."""
     h = hashlib.sha256()
     d = os.path.join(PKG, "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(files if files is not None else os.listdir(d)):
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_sources(kernel_regex: str):
+    """The csrc files a kernel's code can come from: the sources that name its identifier (the
+    leading name of the regex) plus every header of csrc."""
+    m = re.match(r"[A-Za-z_]\w*", kernel_regex)
+    if not m:
+        raise ValueError(f"no kernel name at the start of /{kernel_regex}/")
+    d = os.path.join(PKG, "csrc")
+    out = []
+    for f in sorted(os.listdir(d)):
+        text = open(os.path.join(d, f), encoding="utf-8", errors="replace").read()
+        if f.endswith(".h") or re.search(r"\b" + m.group(0) + r"\b", text):
+            out.append(f)
+    return out
 
 
 def _find(d: str, suffix: str) -> str:
@@ -90,15 +106,17 @@ def write_stats_md(trace_dir: str, cmd: str, out: str, title: str, top: int = 25
     return st
 
 
-def counter_per_dispatch(pmc_dir: str, counter: str, kernel_regex: str):
-    """Values of one counter for every dispatch whose kernel name matches."""
+def counter_per_dispatch(pmc_dir: str, counter: str, kernel_regex: str, grid=None):
+    """Values of one counter for every dispatch whose kernel name matches (and whose grid, in
+    work-items, equals `grid` when given)."""
     rx = re.compile(kernel_regex)
     vals = []
     for r in csv.DictReader(open(_find(pmc_dir, "_counter_collection.csv"))):
         if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
-            vals.append(float(r["Counter_Value"]))
+            if grid is None or int(r["Grid_Size"]) == int(grid):
+                vals.append(float(r["Counter_Value"]))
     if not vals:
-        raise ValueError(f"no {counter} rows for /{kernel_regex}/ in {pmc_dir}")
+        raise ValueError(f"no {counter} rows for /{kernel_regex}/ (grid {grid}) in {pmc_dir}")
     return vals
 
 
@@ -116,25 +134,42 @@ def update_traffic(args):
         fr, _ = copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes, "reduce")
     except ValueError:
         fr = None
-    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
-    write = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel)
-    data = {}
+    grid = getattr(args, "grid", None)
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel, grid)
+    write = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel, grid)
+    data = {"kernels": {}}
     if os.path.exists(args.out):
         data = json.load(open(args.out))
-    h = kernel_source_hash()
-    if data.get("source_hash") != h:
-        data = {"source_hash": h, "kernels": {}}
+    data.pop("source_hash", None)   # figures carry the hash of their own sources
     data["copy_calibration"] = {"bytes": args.copy_bytes, "fetch_factor": ff, "write_factor": fw,
                                 "dispatches": [nf, nw], "read_only_fetch_factor": fr}
     fk, wk = statistics.fmean(fetch), statistics.fmean(write)
-    data["kernels"][args.key] = {
-        "kernel_regex": args.kernel, "dispatches": [len(fetch), len(write)],
+    srcs = kernel_sources(args.kernel)
+    data.setdefault("kernels", {})[args.key] = {
+        "kernel_regex": args.kernel, "grid": grid, "dispatches": [len(fetch), len(write)],
         "fetch_kib": fk, "write_kib": wk,
         "bytes_per_launch": (fk / ff + wk / fw) * 1024.0,
+        "sources": srcs, "source_hash": kernel_source_hash(srcs),
         "fetch_dirs": [args.fetch, args.write]}
     with open(args.out, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(data["kernels"][args.key]))
+
+
+def traffic_entry(path: str, key: str):
+    """HBM bytes per launch stored under `key`, or None if absent or taken on other sources."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entry = json.load(f).get("kernels", {}).get(key)
+    if entry is None or "sources" not in entry:
+        return None
+    try:
+        if kernel_source_hash(entry["sources"]) != entry["source_hash"]:
+            return None
+    except FileNotFoundError:
+        return None
+    return entry["bytes_per_launch"]
 
 
 def counter_table(pmc_dir: str):
@@ -176,6 +211,7 @@ def main():
     for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "key", "out"):
         t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
     t.add_argument("--copy-bytes", dest="copy_bytes", type=int, default=256 << 20)
+    t.add_argument("--grid", type=int, default=None, help="only dispatches of this many work-items")
     c = sub.add_parser("counters")
     c.add_argument("pmc_dir")
     c.add_argument("--cmd", required=True)

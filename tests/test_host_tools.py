@@ -24,10 +24,10 @@ def _write_trace(d, rows):
 def _write_counters(d, rows):
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "x_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
         w.writeheader()
         for r in rows:
-            w.writerow(r)
+            w.writerow({"Grid_Size": 256, **r})
 
 
 def test_short_name_drops_arguments_not_template_parameters():
@@ -72,9 +72,13 @@ def test_traffic_scales_counters_by_the_copy_calibration(tmp_path):
     _write_counters(str(tmp_path / "f"), [
         {"Kernel_Name": "void moe::k_x<1>(A)", "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
         {"Kernel_Name": "void moe::k_x<1>(A)", "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0},
+        {"Kernel_Name": "void moe::k_x<1>(A)", "Grid_Size": 512, "Counter_Name": "FETCH_SIZE",
+         "Counter_Value": 900.0},
         {"Kernel_Name": "void moe::k_y(A)", "Counter_Name": "FETCH_SIZE", "Counter_Value": 7.0}])
     _write_counters(str(tmp_path / "w"), [
-        {"Kernel_Name": "void moe::k_x<1>(A)", "Counter_Name": "WRITE_SIZE", "Counter_Value": 10.0}])
+        {"Kernel_Name": "void moe::k_x<1>(A)", "Counter_Name": "WRITE_SIZE", "Counter_Value": 10.0},
+        {"Kernel_Name": "void moe::k_x<1>(A)", "Grid_Size": 512, "Counter_Name": "WRITE_SIZE",
+         "Counter_Value": 30.0}])
     out = str(tmp_path / "traffic.json")
 
     class Args:
@@ -82,16 +86,31 @@ def test_traffic_scales_counters_by_the_copy_calibration(tmp_path):
     a = Args()
     a.copy_fetch, a.copy_write = str(tmp_path / "cf"), str(tmp_path / "cw")
     a.fetch, a.write = str(tmp_path / "f"), str(tmp_path / "w")
-    a.copy_bytes, a.kernel, a.key, a.out = n, r"k_x<1>", "x", out
+    a.copy_bytes, a.kernel, a.key, a.out, a.grid = n, r"k_x<1>", "x", out, 256
+    P.update_traffic(a)
+    a.grid, a.key = 512, "x512"
     P.update_traffic(a)
     data = json.load(open(out))
-    assert data["source_hash"] == P.kernel_source_hash()
     assert data["copy_calibration"]["fetch_factor"] == pytest.approx(0.5)
     assert data["copy_calibration"]["write_factor"] == pytest.approx(1.0)
     e = data["kernels"]["x"]
     assert e["dispatches"] == [2, 1]
     # mean FETCH 200 KiB / 0.5 + WRITE 10 KiB / 1.0
     assert e["bytes_per_launch"] == pytest.approx((200.0 / 0.5 + 10.0) * 1024)
+    assert data["kernels"]["x512"]["bytes_per_launch"] == pytest.approx((900.0 / 0.5 + 30.0) * 1024)
+    # the figure is tied to the hash of the sources it was taken on
+    assert e["source_hash"] == P.kernel_source_hash(e["sources"])
+    assert P.traffic_entry(out, "x") == pytest.approx(e["bytes_per_launch"])
+    e["source_hash"] = "0" * 16
+    json.dump(data, open(out, "w"))
+    assert P.traffic_entry(out, "x") is None and P.traffic_entry(out, "absent") is None
+
+
+def test_kernel_sources_name_the_defining_file_and_the_headers():
+    from bit_grouped_gemm_amd.profiling import kernel_sources
+    src = kernel_sources("k_dec_b<1, 4>")
+    assert "decode.hip" in src and "moe_internal.h" in src and "attn.hip" not in src
+    assert "attn.hip" in kernel_sources("k_attn_split<128, 8>")
 
 
 def test_kernel_source_hash_is_stable():
