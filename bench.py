@@ -406,8 +406,9 @@ def attention_section(contexts=(4096, 32768, 131072)):
     """GQA decode attention of the model's full-attention layers (16 query heads, 2 KV heads,
     head size 128, 64-token cache blocks), batch 1, at several context lengths. Calls rotate
     over disjoint sequences of one 512 MiB block pool (blocks scattered by a random
-    permutation), so every call reads its keys and values from HBM. Algorithmic bytes: the
-    sequence's keys and values once, the block-table entries, q and out."""
+    permutation), so every call reads its keys and values from HBM; the same sequences are
+    also timed unpacked (one query head per workgroup) and with their blocks in physical order.
+    Algorithmic bytes: the sequence's keys and values once, the block-table entries, q and out."""
     import torch
     from bit_grouped_gemm_amd import attn_gqa as G
     import synth
@@ -431,10 +432,15 @@ def attention_section(contexts=(4096, 32768, 131072)):
               for _ in range(nseq)]
         o = torch.empty((1, Hq, D), dtype=torch.float32, device="cuda")
         ws = G.alloc_workspace(d, 1, S)
+        # the same sequences with their blocks in physical order (a contiguous cache)
+        in_order = [torch.arange(i * nb, (i + 1) * nb, dtype=torch.int32, device="cuda").reshape(1, nb)
+                    for i in range(nseq)]
         res = {}
-        for flags, tag in ((0, "packed"), (G.ATTN_FLAG_UNPACKED, "unpacked")):
-            calls = [(lambda i=i, f=flags: G.decode(d, qs[i].view(torch.int16), kc.view(torch.int16),
-                                                    vc.view(torch.int16), tables[i], lens, S, o, ws, f))
+        for flags, tag, tabs in ((0, "packed", tables), (G.ATTN_FLAG_UNPACKED, "unpacked", tables),
+                                 (0, "packed_blocks_in_order", in_order)):
+            calls = [(lambda i=i, f=flags, t=tabs: G.decode(d, qs[i].view(torch.int16),
+                                                            kc.view(torch.int16), vc.view(torch.int16),
+                                                            t[i], lens, S, o, ws, f))
                      for i in range(nseq)]
             st = replay_stats(calls, max(4, 256 // nseq))
             nbytes = 2.0 * Hkv * S * D * 2 + nb * 4 + Hq * D * 2 + Hq * D * 4

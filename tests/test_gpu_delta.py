@@ -49,7 +49,7 @@ def check(tag, o, s, ref_o, ref_s):
 
 @pytest.mark.parametrize("name,B,T", [("tiny", 3, 7), ("mid", 2, 33), ("full", 1, 1),
                                       ("full", 8, 1), ("full", 2, 64), ("gva", 1, 40),
-                                      ("full", 1, 256)])
+                                      ("full", 1, 256), ("full", 1, 512)])
 def test_recurrence_matches_oracle(name, B, T):
     shape = synth.DELTA_SHAPES[name]
     log(f"[delta] start {name} B={B} T={T}")
@@ -86,3 +86,52 @@ def test_decode_steps_chain_like_one_run():
         outs.append(o1)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(outs, dim=1), o_all) and torch.equal(s, s_all)
+
+
+@pytest.mark.parametrize("with_state", [True, False])
+def test_no_token_passes_the_state_through(with_state):
+    """T = 0: the state comes out unchanged (zero when none is given); no output rows."""
+    import torch
+    from bit_grouped_gemm_amd import delta_rule as DR
+    shape = synth.DELTA_SHAPES["full"]
+    q, k, v, g, beta, s0 = synth.make_delta_inputs(shape, 2, 0, 5)
+    d = DR.desc(shape.num_k_heads, shape.num_v_heads, shape.dk, shape.dv)
+    dev = lambda a, t: torch.from_numpy(np.ascontiguousarray(a).view(t)).to(DEV)  # noqa: E731
+    sin = dev(s0, np.float32) if with_state else None
+    sout = torch.full(s0.shape, float("nan"), dtype=torch.float32, device=DEV)
+    o = torch.empty((2, 0, shape.num_v_heads, shape.dv), dtype=torch.float32, device=DEV)
+    DR.forward(d, dev(q, np.int16), dev(k, np.int16), dev(v, np.int16), dev(g, np.float32),
+               dev(beta, np.float32), sin, sout, o)
+    torch.cuda.synchronize()
+    want = s0 if with_state else np.zeros_like(s0)
+    assert np.array_equal(sout.cpu().numpy(), want)
+
+
+def test_graph_replays_match_eager():
+    """A captured call replayed three times, with eager calls on other buffers in between, gives
+    the eager result bit for bit each time."""
+    import torch
+    from bit_grouped_gemm_amd import delta_rule as DR
+    shape = synth.DELTA_SHAPES["full"]
+    B, T = 2, 3
+    q, k, v, g, beta, s0 = synth.make_delta_inputs(shape, B, T, 12)
+    d = DR.desc(shape.num_k_heads, shape.num_v_heads, shape.dk, shape.dv)
+    dev = lambda a, t: torch.from_numpy(np.ascontiguousarray(a).view(t)).to(DEV)  # noqa: E731
+    args = (dev(q, np.int16), dev(k, np.int16), dev(v, np.int16), dev(g, np.float32),
+            dev(beta, np.float32), dev(s0, np.float32))
+    s_e = torch.empty(s0.shape, device=DEV)
+    o_e = torch.empty((B, T, shape.num_v_heads, shape.dv), device=DEV)
+    DR.forward(d, *args, s_e, o_e)
+    torch.cuda.synchronize()
+    s_g, o_g = torch.empty_like(s_e), torch.empty_like(o_e)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        DR.forward(d, *args, s_g, o_g)
+    for rep in range(3):
+        s_g.fill_(float("nan"))
+        o_g.fill_(float("nan"))
+        DR.forward(d, *args, torch.empty_like(s_e), torch.empty_like(o_e))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(s_g, s_e) and torch.equal(o_g, o_e), rep
