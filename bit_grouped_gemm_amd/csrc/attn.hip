@@ -5,15 +5,20 @@
 // heads sharing two KV heads, over a growing key-value cache) and section "How It Works: Prefill
 // and Decode Strategies" (coalesced key and value cache reads; GQA packing, i.e. the query heads
 // of a KV head sharing its reads; a fixed-block cache layout). Decode attention reads every cached
-// key and value once per token and does a few flops per byte: it is bound by HBM bandwidth, so
-// the work is plain fp32 VALU arithmetic (dot2 on bf16 pairs), not MFMA.
+// key and value once per token and is bound by HBM bandwidth; with G query heads packed per
+// workgroup it does 2G multiply-adds per cached value, which for G = 8 keeps the VALUs about as
+// busy as HBM. So q.K runs on MFMA for packed workgroups (v_mfma_f32_16x16x32_bf16: 16 tokens x
+// the G heads, 32 dimensions per step, exact bf16 products, fp32 sums); P.V and the softmax stay
+// fp32 VALU work.
 //
 // Layout of the work (split over the context, then a merge):
 //  * k_attn_split: one workgroup of 4 waves per (sequence, KV head, span of the context) with
 //    all G query heads of that KV head (packed). A span is a run of chunks; a token's key row of
 //    D bf16 is read by D/8 consecutive lanes, 16 bytes each, so one wave instruction reads whole
 //    rows (64 * 16 bytes); the block table is read per token, so chunks may span blocks of any
-//    placement. Per chunk: scores to LDS, each head's running maximum and the chunk's
+//    placement (with MFMA scores, a lane reads 16 bytes of a token row per MFMA step instead:
+//    four lanes cover 64 contiguous bytes of each of 16 rows). Per chunk: scores to LDS, each
+//    head's running maximum and the chunk's
 //    exponentials (fp32, online softmax: earlier sums are rescaled by exp(m_old - m_new)), then
 //    P.V with each lane accumulating 8 dimensions of G heads. A chunk is sized so that every
 //    lane requests all its key and value rows of the chunk at once, and the next chunk's keys
@@ -92,6 +97,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   constexpr int TPI = 64 / LPT;  // tokens per wave instruction
   constexpr int TPB = 4 * TPI;   // tokens per workgroup step
   constexpr int C = attn_chunk<D, U>();  // U steps: every row of a chunk requested up front
+  // q.K on MFMA (16 x 16 x 32 bf16, HPW of the 16 columns used) for packed workgroups with
+  // long chunks; the VALU dot products otherwise
+  constexpr bool kMM = HPW >= 4 && U == 8;
+  constexpr int NJ = D / 32;     // MFMAs per 16-token tile (32 dimensions each)
+  static_assert(!kMM || (C / 64) * NJ == U, "a lane's key loads per chunk are the same");
   __shared__ __attribute__((aligned(16))) float sc[HPW * C];       // scores, then probabilities
   __shared__ __attribute__((aligned(16))) float wacc[4 * HPW * D];  // per-wave sums
   __shared__ float st[3 * HPW];   // per head: running max, running sum, this chunk's rescale
@@ -118,15 +128,41 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   };
   // token of step u of the chunk at c0, clamped into the span (the clamped rows are not used)
   auto tok = [&](int c0, int u) { return min(c0 + u * TPB + wave * TPI + tsub, t1 - 1); };
+  // MFMA scores (kMM): wave w takes tokens [w*C/4, (w+1)*C/4) of a chunk as 16-token tiles;
+  // key load u = tile * NJ + j is this lane's 16 bytes of token (lane % 16) of the tile at
+  // dimensions 32j + 8*(lane / 16): the A operand of v_mfma_f32_16x16x32_bf16 (rows = tokens,
+  // k = 32 dimensions), whose B operand is q^T (columns = the HPW heads, the rest zero).
+  auto krow_mm = [&](int c0, int u) -> const uint4* {
+    const int tt = u / NJ, j = u % NJ;
+    const int jt = min(c0 + wave * (C / 4) + tt * 16 + (lane & 15), t1 - 1);
+    int blk = trow[jt >> a.bs_shift];
+    blk = blk < 0 ? 0 : (blk >= a.nblocks ? a.nblocks - 1 : blk);
+    return reinterpret_cast<const uint4*>(
+        a.kc + ((((size_t)blk * a.Hkv + g) << a.bs_shift) + (jt & bs_mask)) * D + 32 * j +
+        8 * (lane >> 4));
+  };
+  auto krow = [&](int c0, int u) -> const uint4* {
+    if constexpr (kMM) return krow_mm(c0, u);
+    else return row(a.kc, tok(c0, u));
+  };
   uint4 kv[U], vv[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) kv[u] = *row(a.kc, tok(t0, u));
+  for (int u = 0; u < U; ++u) kv[u] = *krow(t0, u);
 #pragma unroll
   for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(t0, u));
-  uint4 qv[HPW];
+  uint4 qv[kMM ? NJ : HPW];
+  if constexpr (kMM) {
+    const int hq = lane & 15;  // B operand: head hq, dimensions 32j + 8*(lane / 16) .. + 8
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
-    qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
+    for (int j = 0; j < NJ; ++j)
+      qv[j] = hq < HPW ? *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hq) * D +
+                                                         32 * j + 8 * (lane >> 4))
+                       : make_uint4(0u, 0u, 0u, 0u);
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+      qv[hh] = *reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.Hq + h0 + hh) * D + dsl * 8);
+  }
   if (tid < HPW) {
     st[tid] = -INFINITY;
     st[HPW + tid] = 0.0f;
@@ -141,27 +177,47 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     const int n = min(C, t1 - c0);           // tokens of this chunk
     const bool more = c0 + C < t1;
     // ---- scores: q_h . k_j for the chunk's tokens, scaled
+    if constexpr (kMM) {
+      // D[token][head] of each 16-token tile: lane l holds head l % 16 for tokens
+      // 4*(l / 16) + i of the tile, i < 4
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = u * TPB + wave * TPI + tsub;
-      float t[HPW];
+      for (int tt = 0; tt < C / 64; ++tt) {
+        f32x4_t d4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
-        d = dot2_bf16(kv[u].y, qv[hh].y, d);
-        d = dot2_bf16(kv[u].z, qv[hh].z, d);
-        d = dot2_bf16(kv[u].w, qv[hh].w, d);
-        t[hh] = group_sum<LPT>(d);
+        for (int j = 0; j < NJ; ++j)
+          d4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[tt * NJ + j]),
+                                                       __builtin_bit_cast(bf16x8_t, qv[j]), d4, 0, 0, 0);
+        const int hq = lane & 15;
+        const int s0 = wave * (C / 4) + tt * 16 + 4 * (lane >> 4);
+        if (hq < HPW) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s0 + i < n) sc[hq * C + s0 + i] = d4[i] * a.scale;
+        }
       }
-      float val = 0.0f;
+    } else {
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
-        if (dsl == hh) val = t[hh];
-      if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
+      for (int u = 0; u < U; ++u) {
+        const int s = u * TPB + wave * TPI + tsub;
+        float t[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          float d = dot2_bf16(kv[u].x, qv[hh].x, 0.0f);
+          d = dot2_bf16(kv[u].y, qv[hh].y, d);
+          d = dot2_bf16(kv[u].z, qv[hh].z, d);
+          d = dot2_bf16(kv[u].w, qv[hh].w, d);
+          t[hh] = group_sum<LPT>(d);
+        }
+        float val = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          if (dsl == hh) val = t[hh];
+        if (s < n && dsl < HPW) sc[dsl * C + s] = val * a.scale;
+      }
     }
     if (more) {   // the keys are used: request the next chunk's
 #pragma unroll
-      for (int u = 0; u < U; ++u) kv[u] = *row(a.kc, tok(c0 + C, u));
+      for (int u = 0; u < U; ++u) kv[u] = *krow(c0 + C, u);
     }
     __syncthreads();
 

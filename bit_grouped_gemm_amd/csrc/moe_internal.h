@@ -108,6 +108,7 @@ hipError_t launch_stream_read(const void* p, size_t bytes, int workgroups, uint3
 // ------------------------------------------------------------------ device helpers
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
