@@ -7,20 +7,24 @@
 // of a KV head sharing its reads; a fixed-block cache layout). Decode attention reads every cached
 // key and value once per token and is bound by HBM bandwidth; with G query heads packed per
 // workgroup it does 2G multiply-adds per cached value, which for G = 8 keeps the VALUs about as
-// busy as HBM. So q.K runs on MFMA for packed workgroups (v_mfma_f32_16x16x32_bf16: 16 tokens x
-// the G heads, 32 dimensions per step, exact bf16 products, fp32 sums); P.V and the softmax stay
-// fp32 VALU work.
+// busy as HBM. So packed workgroups run both products on MFMA (v_mfma_f32_16x16x32_bf16, the G
+// heads as 16 columns): q.K per 16-token tile, 32 dimensions per step (exact bf16 products, fp32
+// sums), and P.V per 16-dimension tile, 32 tokens per step, with the fp32 probabilities entering
+// as two bf16 parts (hi = RNE(p), lo = RNE(p - hi)) so that about 16 of their significant bits
+// take part; the softmax stays fp32 VALU work.
 //
 // Layout of the work (split over the context, then a merge):
 //  * k_attn_split: one workgroup of 4 waves per (sequence, KV head, span of the context) with
 //    all G query heads of that KV head (packed). A span is a run of chunks; a token's key row of
 //    D bf16 is read by D/8 consecutive lanes, 16 bytes each, so one wave instruction reads whole
 //    rows (64 * 16 bytes); the block table is read per token, so chunks may span blocks of any
-//    placement (with MFMA scores, a lane reads 16 bytes of a token row per MFMA step instead:
+//    placement (for MFMA scores a lane reads 16 bytes of a token row per MFMA step instead:
 //    four lanes cover 64 contiguous bytes of each of 16 rows). Per chunk: scores to LDS, each
-//    head's running maximum and the chunk's
-//    exponentials (fp32, online softmax: earlier sums are rescaled by exp(m_old - m_new)), then
-//    P.V with each lane accumulating 8 dimensions of G heads. A chunk is sized so that every
+//    head's running maximum and the chunk's exponentials (fp32, online softmax: earlier sums are
+//    rescaled by exp(m_old - m_new)), then P.V: on MFMA (packed) each wave owns D/4 dimensions
+//    of every head, with the chunk's value rows staged in LDS; on VALU each lane accumulates 8
+//    dimensions of the workgroup's heads, summed over lanes and waves at the end. A chunk is
+//    sized so that every
 //    lane requests all its key and value rows of the chunk at once, and the next chunk's keys
 //    (values) are requested as soon as the current ones have been used, so a workgroup keeps a
 //    chunk's rows in flight while it computes. The span's (max, sum, acc) per head is stored.
@@ -102,8 +106,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   constexpr bool kMM = HPW >= 4 && U == 8;
   constexpr int NJ = D / 32;     // MFMAs per 16-token tile (32 dimensions each)
   static_assert(!kMM || (C / 64) * NJ == U, "a lane's key loads per chunk are the same");
+  // MFMA path: the chunk's value rows in LDS, row-major with a pitch of D + 4 bf16, so that the
+  // transposed operand reads of P.V (8 rows apart per lane group) fall in distinct banks
+  constexpr int VP = D + 4;
   __shared__ __attribute__((aligned(16))) float sc[HPW * C];       // scores, then probabilities
-  __shared__ __attribute__((aligned(16))) float wacc[4 * HPW * D];  // per-wave sums
+  __shared__ __attribute__((aligned(16))) float wacc[kMM ? 1 : 4 * HPW * D];  // per-wave sums
+  __shared__ __attribute__((aligned(16))) uint16_t vl[kMM ? C * VP : 1];      // value rows
   __shared__ float st[3 * HPW];   // per head: running max, running sum, this chunk's rescale
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,11 +175,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     st[tid] = -INFINITY;
     st[HPW + tid] = 0.0f;
   }
-  float acc[HPW][8];
+  // VALU P.V: 8 dimensions of the HPW heads per lane. MFMA P.V: the wave's D/64 tiles of 16
+  // dimensions, O^T[dim][head] (lane l: head l % 16, dimensions 4*(l / 16) + i of the tile)
+  constexpr int ND = kMM ? D / 64 : 1;
+  float acc[kMM ? 1 : HPW][8];
+  f32x4_t oacc[ND];
+  if constexpr (kMM) {
 #pragma unroll
-  for (int hh = 0; hh < HPW; ++hh)
+    for (int dt = 0; dt < ND; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+  }
 
   for (int c0 = t0; c0 < t1; c0 += C) {
     const int n = min(C, t1 - c0);           // tokens of this chunk
@@ -219,6 +236,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) kv[u] = *krow(c0 + C, u);
     }
+    if constexpr (kMM) {  // the value rows to LDS, then the next chunk's requested
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = u * TPB + wave * TPI + tsub;
+        uint2* dst = reinterpret_cast<uint2*>(vl + s * VP + dsl * 8);
+        dst[0] = make_uint2(vv[u].x, vv[u].y);
+        dst[1] = make_uint2(vv[u].z, vv[u].w);
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(c0 + C, u));
+      }
+    }
     __syncthreads();
 
     // ---- per head: new running maximum, exponentials (kept in place), sums
@@ -243,6 +273,46 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     }
     __syncthreads();
 
+    if constexpr (kMM) {
+      // ---- P.V on MFMA: O^T[dim][head] += V^T[dim][tokens] P^T[tokens][head] over 32-token
+      // blocks; P (fp32) enters as two bf16 parts, hi = RNE(p) and lo = RNE(p - hi), so that the
+      // products keep about 16 significant bits of p
+      const int hq = lane & 15;
+      const float f = hq < HPW ? st[2 * HPW + hq] : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] *= f;
+#pragma unroll
+      for (int tb = 0; tb < C / 32; ++tb) {
+        const int t8 = tb * 32 + 8 * (lane >> 4);   // this lane's 8 tokens of the block
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p0 = 0.0f, p1 = 0.0f;
+          if (hq < HPW) {
+            p0 = t8 + 2 * e < n ? sc[hq * C + t8 + 2 * e] : 0.0f;
+            p1 = t8 + 2 * e + 1 < n ? sc[hq * C + t8 + 2 * e + 1] : 0.0f;
+          }
+          ph[e] = pack_bf16x2(p0, p1);
+          pl[e] = pack_bf16x2(p0 - bf16_to_f32(ph[e] & 0xFFFFu), p1 - bf16_to_f32(ph[e] >> 16));
+        }
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          const int dim = (wave * ND + dt) * 16 + hq;   // A operand: row = this dimension
+          uint32_t vw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vw[e] = (uint32_t)vl[(t8 + 2 * e) * VP + dim] |
+                    ((uint32_t)vl[(t8 + 2 * e + 1) * VP + dim] << 16);
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(vw[0], vw[1], vw[2], vw[3]));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, oacc[dt], 0, 0, 0);
+        }
+      }
+      __syncthreads();   // the next chunk's scores and values overwrite sc, st and vl
+      continue;
+    }
     // ---- P.V: each lane accumulates its 8 dimensions for the HPW heads
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -276,6 +346,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     __syncthreads();   // the next chunk's scores overwrite sc and st
   }
 
+  const size_t rec = (size_t)(D + 4);
+  if constexpr (kMM) {   // each wave holds whole dimensions of every head: no reduction
+    const int hq = lane & 15;
+    float* part = a.part + (((size_t)b * a.Hq + h0) * a.nspans + blockIdx.x) * rec;
+    if (hq < HPW) {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const int d0 = (wave * ND + dt) * 16 + 4 * (lane >> 4);
+        *reinterpret_cast<float4*>(part + hq * a.nspans * rec + 4 + d0) =
+            make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+      }
+    }
+    if (tid < HPW) {
+      part[tid * a.nspans * rec + 0] = st[tid];
+      part[tid * a.nspans * rec + 1] = st[HPW + tid];
+    }
+    return;
+  }
   // sum over the wave's token groups (lanes with the same dimensions), then over the waves
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1)
@@ -290,7 +378,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
       for (int e = 0; e < 8; ++e) wacc[(wave * HPW + hh) * D + dsl * 8 + e] = acc[hh][e];
   }
   __syncthreads();
-  const size_t rec = (size_t)(D + 4);
   float* part = a.part + (((size_t)b * a.Hq + h0) * a.nspans + blockIdx.x) * rec;
   for (int i = tid; i < HPW * D; i += kAttnThreads) {
     const int hh = i / D, d = i % D;
