@@ -79,9 +79,9 @@ __global__ __launch_bounds__(256) void k_delta_rule_tok(DeltaArgs a) {
   constexpr int RPW = 64 / LPR;   // rows per wave
   constexpr int RPG = 4 * RPW;    // rows per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.x, b = blockIdx.z;  // head fastest: with Hv a multiple of 8 a head's row blocks share an XCD (and its L2)
   const int i = j / (a.Hv / a.Hk);                         // the q/k head of value head j
-  const int r = blockIdx.x * RPG + wave * RPW + lane / LPR;  // this lane's state row
+  const int r = blockIdx.y * RPG + wave * RPW + lane / LPR;  // this lane's state row
   const int c0 = (lane % LPR) * 4;                          // its first state column
   const bool lead = (lane % LPR) == 0;
 
@@ -151,9 +151,9 @@ __global__ __launch_bounds__(2 * DK) void k_delta_rule_blk(DeltaArgs a) {
   __shared__ float vs[TB * kDeltaRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.x, b = blockIdx.z;  // head fastest: with Hv a multiple of 8 a head's row blocks share an XCD (and its L2)
   const int i = j / (a.Hv / a.Hk);                 // the q/k head of value head j
-  const int r0 = blockIdx.x * kDeltaRows;
+  const int r0 = blockIdx.y * kDeltaRows;
   const int rl = wave * RPW + lane / LPR;          // this lane's row in the workgroup
   const int r = r0 + rl;
   const int c0 = (lane % LPR) * 8;                 // its first state column
@@ -326,12 +326,12 @@ extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t*
   DeltaArgs a{q, k, v, g, beta, state_in, state_out, o, Hk, Hv, dv, T, desc->scale, desc->eps};
   if (T < kDeltaBlockFrom) {
     const int rpg = 4 * (64 / (dk / 4));
-    const dim3 grid(dv / rpg, Hv, batch);
+    const dim3 grid(Hv, dv / rpg, batch);
     if (dk == 64) hipLaunchKernelGGL((k_delta_rule_tok<64>), grid, dim3(256), 0, s, a);
     else if (dk == 128) hipLaunchKernelGGL((k_delta_rule_tok<128>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_delta_rule_tok<256>), grid, dim3(256), 0, s, a);
   } else {
-    const dim3 grid(dv / kDeltaRows, Hv, batch);  // workgroups of 2 * dk threads
+    const dim3 grid(Hv, dv / kDeltaRows, batch);  // workgroups of 2 * dk threads
     if (dk == 64) hipLaunchKernelGGL((k_delta_rule_blk<64>), grid, dim3(128), 0, s, a);
     else if (dk == 128) hipLaunchKernelGGL((k_delta_rule_blk<128>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_delta_rule_blk<256>), grid, dim3(512), 0, s, a);
