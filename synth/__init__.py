@@ -1,5 +1,6 @@
 """Seeded synthetic inputs (shared by the oracle tests and the HIP path): the MoE layer, GQA
-decode attention over a block-paged KV cache, and the gated delta-rule recurrence.
+decode attention over a block-paged KV cache, the gated delta-rule recurrence, and the greedy
+decode step's LM head and token embedding.
 
 These modules only draw random numbers and store them in the storage formats of the
 operations. They hold none of the operations' arithmetic.
@@ -9,3 +10,4 @@ from .moe_inputs import (  # noqa: F401
 )
 from .attn_inputs import AttnShape, ATTN_SHAPES, make_attn_inputs  # noqa: F401
 from .delta_inputs import DeltaShape, DELTA_SHAPES, make_delta_inputs  # noqa: F401
+from .head_inputs import VOCAB, make_head  # noqa: F401
