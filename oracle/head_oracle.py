@@ -42,7 +42,10 @@ def greedy(logits) -> np.ndarray:
 def near_tie(logits, gap: float = 1e-4) -> np.ndarray:
     """Rows whose two largest logits are closer than `gap` (the argmax may then differ between
     two correct evaluations in different summation orders)."""
-    top2 = -np.sort(-np.asarray(logits), axis=1)[:, :2]
+    lg = np.asarray(logits)
+    if lg.shape[1] < 2:      # a single entry has no rival
+        return np.zeros(0, dtype=np.int64)
+    top2 = -np.sort(-lg, axis=1)[:, :2]
     return np.nonzero(top2[:, 0] - top2[:, 1] < gap)[0]
 
 

@@ -22,6 +22,7 @@ def declared_functions():
 
 ATTN_HEADER = os.path.join(ROOT, "include", "attn_gqa.h")
 DELTA_HEADER = os.path.join(ROOT, "include", "delta_rule.h")
+GREEDY_HEADER = os.path.join(ROOT, "include", "greedy_head.h")
 
 
 def declared_in(path):
@@ -34,10 +35,10 @@ def declared_in(path):
 def test_every_header_is_exported():
     """Each header's declarations are exactly its binding's export list, and the library
     exports every one of them."""
-    from bit_grouped_gemm_amd import attn_gqa, delta_rule
+    from bit_grouped_gemm_amd import attn_gqa, delta_rule, greedy_head
     lib = ctypes.CDLL(M.LIB_PATH)
     for path, exports in ((HEADER, M.EXPORTS), (ATTN_HEADER, attn_gqa.EXPORTS),
-                          (DELTA_HEADER, delta_rule.EXPORTS)):
+                          (DELTA_HEADER, delta_rule.EXPORTS), (GREEDY_HEADER, greedy_head.EXPORTS)):
         names = declared_in(path)
         assert set(names) == set(exports), path
         for n in names:
@@ -217,3 +218,25 @@ def test_workspace_layout_export():
             assert total - y >= (T * 8 + T) * 2048 * 4
     arr = (C.c_size_t * 14)()
     assert M.lib().moe_debug_workspace_layout(C.byref(d), 4, 4, arr, 14) == M.MOE_INVALID_ARG
+
+
+def test_greedy_step_rejections():
+    """Host-side checks of moe_greedy_next_input (no kernel is enqueued on these paths)."""
+    from bit_grouped_gemm_amd import greedy_head as Gh
+    L = Gh._lib()
+    w = M.W4(FAKE, FAKE, FAKE)
+    ws = Gh.workspace_bytes(151936, 1)
+    assert ws >= 151936 * 4 and Gh.workspace_bytes(0, 1) == 0 and Gh.workspace_bytes(10, 17) == 0
+
+    def call(V=1000, H=2048, T=1, x=FAKE, tok=FAKE, xn=FAKE, wsp=FAKE, nbytes=1 << 30, head=w):
+        return L.moe_greedy_next_input(ctypes.byref(head), ctypes.byref(w), V, H, x, T, tok, xn,
+                                       wsp, nbytes, None)
+    assert call(H=3072) == M.MOE_UNSUPPORTED
+    assert call(H=4096, T=9) == M.MOE_UNSUPPORTED
+    assert call(T=0) == M.MOE_INVALID_ARG and call(T=17) == M.MOE_INVALID_ARG
+    assert call(V=0) == M.MOE_INVALID_ARG
+    assert call(x=None) == M.MOE_INVALID_ARG and call(tok=None) == M.MOE_INVALID_ARG
+    assert call(x=FAKE + 2) == M.MOE_INVALID_ARG           # x must be 16-byte aligned
+    assert call(wsp=FAKE + 16) == M.MOE_INVALID_ARG        # workspace 256-byte aligned
+    assert call(nbytes=16) == M.MOE_WORKSPACE_TOO_SMALL
+    assert call(head=M.W4(None, FAKE, FAKE)) == M.MOE_INVALID_ARG

@@ -39,6 +39,7 @@ def test_argmax_takes_the_lowest_index_among_equal_maxima():
 def test_near_tie_reports_close_top_two():
     lg = np.array([[1.0, 1.00005, 0.0], [1.0, 2.0, 0.0]])
     assert Hd.near_tie(lg).tolist() == [0]
+    assert Hd.near_tie(np.array([[3.0], [1.0]])).tolist() == []   # one entry: no rival
 
 
 def test_logits_match_a_scalar_loop():
