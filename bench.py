@@ -57,7 +57,7 @@ def parse():
                     help="oracle CPU-baseline budget of the decode leg")
     ap.add_argument("--only", choices=["decode_t1", "decode_t8", "prefill_uniform",
                                        "prefill_skewed", "stack", "copy", "peaks", "attn",
-                                       "delta"])
+                                       "delta", "greedy"])
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--attn-contexts", default="4096,32768,131072",
                     help="context lengths of the attention section (comma-separated)")
@@ -106,6 +106,16 @@ class Pool:
         self.tok = torch.from_numpy(self.tok_host.view(np.int16)).cuda()
         self.prefill_host = [synth.make_tokens(s, T_PREFILL, seed=0, stream=10 + j) for j in range(2)]
         self.prefill = [torch.from_numpy(x.view(np.int16)).cuda() for x in self.prefill_host]
+
+    def head(self, seed: int):
+        """A device LM head and embedding of the default vocabulary (built once per seed)."""
+        if not hasattr(self, "_heads"):
+            self._heads = {}
+        if seed not in self._heads:
+            import synth
+            from bit_grouped_gemm_amd import greedy_head as Gh
+            self._heads[seed] = Gh.upload_head(synth.make_head(synth.VOCAB, self.shape.H, seed))
+        return self._heads[seed]
 
     def token_slice(self, i, T):
         n = self.tok.shape[0]
@@ -393,13 +403,52 @@ def stack_section(pool: Pool):
     st = replay_stats([lambda: stack.forward(r1, x1, ws1)], DECODE_STEPS_STACK, 8)
     ms_step = st["mean"]
     assert torch.isfinite(r1).all().item()
+    # the whole greedy decode step: the 40 layers, then the LM head, the argmax and the chosen
+    # token's embedding written into the input slot the next step reads
+    from bit_grouped_gemm_amd import greedy_head as Gh
+    hd = pool.head(0)
+    wsg = Gh.alloc_workspace(hd.V, 1)
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    xg = pool.token_slice(5, 1).clone()
+
+    def step():
+        stack.forward(r1, xg, ws1)
+        Gh.next_input(hd, xg, tok, xg, wsg)
+    stg = replay_stats([step], DECODE_STEPS_STACK, 8)
+    assert 0 <= int(tok.item()) < hd.V
     return {"layers": len(pool.layers), "prefill_tokens": T_PREFILL, "chunk": CHUNK,
             "prefill_ms": prefill_ms, "prefill_tokens_per_s": T_PREFILL / (prefill_ms * 1e-3),
             "decode_steps": DECODE_STEPS_STACK, "decode_ms_per_token": ms_step,
             "decode_tokens_per_s": 1.0 / (ms_step * 1e-3),
             "decode_latency_us": pct_us(st),
             "decode_hbm_frac": len(pool.layers) * decode_layer_bytes(s, 1, s.K) / (ms_step * 1e-3)
-            / 1e9 / HBM_PEAK_GBS}
+            / 1e9 / HBM_PEAK_GBS,
+            "greedy_decode": {"what": "40 layers + LM head + argmax + embedding of the token into "
+                                      "the input slot, per token (vocabulary %d)" % hd.V,
+                              "ms_per_token": stg["mean"], "tokens_per_s": 1.0 / (stg["mean"] * 1e-3),
+                              "latency_us": pct_us(stg)}}
+
+
+def greedy_section(pool: Pool):
+    """The greedy step alone at T = 1: the 4-bit LM head over the vocabulary (151,936 x 2048),
+    the argmax and the embedding row. Calls alternate between two heads (350 MB together, more
+    than the memory-side cache). Algorithmic bytes: the head's packed words, scales and biases
+    once, x, the token's embedding row (packed) and the next input."""
+    import torch
+    from bit_grouped_gemm_amd import greedy_head as Gh
+    heads = [pool.head(0), pool.head(1)]
+    V, H = heads[0].V, heads[0].H
+    ws = Gh.alloc_workspace(V, 1)
+    xs = [pool.token_slice(7 + i, 1).clone() for i in range(2)]
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    xn = torch.empty_like(xs[0])
+    calls = [(lambda h=h, x=x: Gh.next_input(h, x, tok, xn, ws)) for h, x in zip(heads, xs)]
+    st = replay_stats(calls, 64)
+    nbytes = V * H // 2 + 2 * 2 * V * (H // 64) + H * 2 + H // 2 + 4 * (H // 64) + H * 2
+    gbs = nbytes / (st["mean"] * 1e-3) / 1e9
+    return {"workload": f"greedy step, T=1: 4-bit LM head {V} x {H}, argmax, embedding",
+            "us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st), "bytes_per_call": nbytes,
+            "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
 def attention_section(contexts=(4096, 32768, 131072)):
@@ -652,6 +701,9 @@ def main():
         r = stack_section(pool)
         log(f"stack: {r}")
         return
+    if args.only == "greedy":
+        log(f"greedy step: {json.dumps(greedy_section(pool))}")
+        return
 
     peaks = measured_peaks()
     log(f"measured peaks: copy {peaks['copy_gbs']:.0f} GB/s, read {peaks['read_gbs']:.0f} GB/s, "
@@ -683,12 +735,16 @@ def main():
             f"({p['tokens_per_s'] / 1e6:.2f} M tok/s, {tf:.0f} TFLOP/s); phases {p['phases_us']}")
     st = stack_section(pool)
     log(f"stack ({st['layers']} layers): prefill {st['prefill_tokens_per_s']:.0f} tok/s, "
-        f"decode {st['decode_tokens_per_s']:.0f} tok/s ({st['decode_ms_per_token'] * 1e3:.0f} us/token)")
+        f"decode {st['decode_tokens_per_s']:.0f} tok/s ({st['decode_ms_per_token'] * 1e3:.0f} us/token); "
+        f"with the greedy step {st['greedy_decode']['tokens_per_s']:.0f} tok/s")
     attn = attention_section(contexts)
     for k_, r_ in attn["contexts"].items():
         log(f"decode attention {k_}: {r_['packed']['us_per_call']:.1f} us "
             f"({r_['packed']['hbm_frac'] * 100:.1f} % of HBM), unpacked "
             f"{r_['unpacked']['us_per_call']:.1f} us")
+    greedy = greedy_section(pool)
+    log(f"greedy step (LM head {greedy['bytes_per_call'] / 1e6:.0f} MB): {greedy['us_per_call']:.1f} us "
+        f"({greedy['hbm_frac'] * 100:.1f} % of HBM)")
     delta = delta_section()
     for k_, r_ in delta["cases"].items():
         log(f"delta rule {k_}: {r_['us_per_call']:.2f} us ({r_['hbm_frac'] * 100:.1f} % of HBM)")
@@ -729,6 +785,7 @@ def main():
         "stack_40_layers": st,
         "gqa_decode_attention": attn,
         "gated_delta_rule": delta,
+        "greedy_step": greedy,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -26,7 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kHeadWaves = 4;
-constexpr int kHeadMaxWG = 1024;
+constexpr int kHeadMaxWG = 2048;
 constexpr int kHeadMaxT = 16;
 
 struct HeadArgs {
