@@ -448,7 +448,8 @@ def greedy_section(pool: Pool):
     gbs = nbytes / (st["mean"] * 1e-3) / 1e9
     return {"workload": f"greedy step, T=1: 4-bit LM head {V} x {H}, argmax, embedding",
             "us_per_call": st["mean"] * 1e3, "latency_us": pct_us(st), "bytes_per_call": nbytes,
-            "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+            "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "logits_kernel_traffic": measured_traffic(f"greedy@v{V}_t1")}
 
 
 def attention_section(contexts=(4096, 32768, 131072)):
