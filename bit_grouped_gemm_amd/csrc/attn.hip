@@ -87,8 +87,9 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Tokens of one chunk: U wave-instruction steps of the workgroup, so that each lane requests all
 // of its key and value rows of the chunk at once (one memory round trip per chunk). U = 8 for
-// long contexts; U = 2 (chunks a quarter as long) when the long chunks would leave the grid
-// short of workgroups.
+// long contexts; when the long chunks would leave the grid short of workgroups, U = 4 for
+// packed workgroups (64 tokens at D = 128, still whole 16-token MFMA tiles per wave) and U = 2
+// otherwise.
 template <int D, int U>
 __host__ __device__ constexpr int attn_chunk() {
   return U * 4 * (64 / (D / 8));   // U steps of 4 waves x (64 / (D/8)) tokens
@@ -103,9 +104,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   constexpr int C = attn_chunk<D, U>();  // U steps: every row of a chunk requested up front
   // q.K on MFMA (16 x 16 x 32 bf16, HPW of the 16 columns used) for packed workgroups with
   // long chunks; the VALU dot products otherwise
-  constexpr bool kMM = HPW >= 4 && U == 8;
   constexpr int NJ = D / 32;     // MFMAs per 16-token tile (32 dimensions each)
-  static_assert(!kMM || (C / 64) * NJ == U, "a lane's key loads per chunk are the same");
+  constexpr bool kMM = HPW >= 4 && C % 64 == 0 && (C / 64) * NJ == U;  // same loads per lane
   // MFMA path: the chunk's value rows in LDS, row-major with a pitch of D + 4 bf16, so that the
   // transposed operand reads of P.V (8 rows apart per lane group) fall in distinct banks
   constexpr int VP = D + 4;
@@ -484,12 +484,14 @@ struct AttnPlan {
 
 int chunk_tokens(int D, int u) {
   if (u == 8) return D == 64 ? attn_chunk<64, 8>() : D == 128 ? attn_chunk<128, 8>() : attn_chunk<256, 8>();
+  if (u == 4) return D == 64 ? attn_chunk<64, 4>() : D == 128 ? attn_chunk<128, 4>() : attn_chunk<256, 4>();
   return D == 64 ? attn_chunk<64, 2>() : D == 128 ? attn_chunk<128, 2>() : attn_chunk<256, 2>();
 }
 
-// Chunks of attn_chunk<D, 8>() tokens (256, 128 or 64 for D = 64, 128, 256), or a quarter of
-// that when the long chunks would give fewer than kAttnTargetWorkgroups workgroups. Spans take as
-// many chunks as it needs to keep the grid near the target (packed or unpacked) in workgroups.
+// Chunks of attn_chunk<D, 8>() tokens (256, 128 or 64 for D = 64, 128, 256), or shorter ones
+// when those would give fewer than kAttnTargetWorkgroups workgroups: half as long for packed
+// workgroups with D <= 128 (the MFMA path), a quarter otherwise. Spans take as many chunks as it
+// needs to keep the grid near the target (packed or unpacked) in workgroups.
 AttnPlan attn_plan(const attn_gqa_desc_t* d, int B, int max_len, bool unpacked) {
   AttnPlan p{};
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -498,7 +500,8 @@ AttnPlan attn_plan(const attn_gqa_desc_t* d, int B, int max_len, bool unpacked) 
   const int64_t groups = (int64_t)(B > 0 ? B : 1) * (d->num_q_heads / p.hpw);
   const int64_t len = max_len > 0 ? max_len : 1;
   p.u = 8;
-  if (groups * ((len + chunk_tokens(D, 8) - 1) / chunk_tokens(D, 8)) < kAttnTargetWorkgroups) p.u = 2;
+  if (groups * ((len + chunk_tokens(D, 8) - 1) / chunk_tokens(D, 8)) < kAttnTargetWorkgroups)
+    p.u = (p.hpw >= 4 && D <= 128) ? 4 : 2;   // packed: 64-token chunks keep the MFMA path
   p.chunk = chunk_tokens(D, p.u);
   const int64_t nchunks = (len + p.chunk - 1) / p.chunk;
   const int64_t target = p.hpw == 1 ? kAttnTargetWorkgroupsUnpacked : kAttnTargetWorkgroups;
@@ -580,6 +583,7 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
 #define ATTN_SPLIT_U(DV, HV)                    \
   do {                                          \
     if (p.u == 8) ATTN_SPLIT(DV, HV, 8);        \
+    else if (p.u == 4) ATTN_SPLIT(DV, HV, 4);   \
     else ATTN_SPLIT(DV, HV, 2);                 \
   } while (0)
 #define ATTN_SPLIT_D(HV)                        \
