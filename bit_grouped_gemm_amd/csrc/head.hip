@@ -26,7 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kHeadWaves = 4;
-constexpr int kHeadMaxWG = 2048;
+constexpr int kHeadMaxWG = 2048;   // a multiple of 256 (k_head_pick reads kHeadMaxWG / 256 each)
 constexpr int kHeadMaxT = 16;
 
 struct HeadArgs {
@@ -177,13 +177,19 @@ __global__ __launch_bounds__(256) void k_head_pick(HeadArgs a, int nwg) {
   const int t = blockIdx.x, tid = threadIdx.x;
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int w = tid; w < nwg; w += 256) {
-    const int2 p = a.part[(size_t)w * a.T + t];
-    if (better(__int_as_float(p.x), p.y, bv, bi)) {
-      bv = __int_as_float(p.x);
-      bi = p.y;
-    }
+  constexpr int kPer = kHeadMaxWG / 256;   // partials per thread, all requested at once
+  int2 pv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int w = tid + 256 * i;
+    pv[i] = w < nwg ? a.part[(size_t)w * a.T + t] : make_int2(__float_as_int(-INFINITY), INT_MAX);
   }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (better(__int_as_float(pv[i].x), pv[i].y, bv, bi)) {
+      bv = __int_as_float(pv[i].x);
+      bi = pv[i].y;
+    }
   bv_s[tid] = bv;
   bi_s[tid] = bi;
   __syncthreads();
