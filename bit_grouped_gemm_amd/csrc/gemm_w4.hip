@@ -227,7 +227,8 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
       }
     }
   };
-  // scale/bias of chunk (c0 + k), c0 the unrolled step's first chunk (SU: words already shifted)
+  // scale/bias of chunk c0 + k, c0 the loop body's first chunk (SU: words already shifted;
+  // not SU: k < kNB is the chunk's slot)
   auto scales_of = [&](int k) -> SChunk<NC> {
     SChunk<NC> r;
     if constexpr (SU) {
@@ -280,22 +281,27 @@ __device__ __forceinline__ void gemm_block(const GemmParams& p, const LdsArrays&
     issue(k, k, bq[k]);
     issue_s(k, k);
   }
-  for (int c = 0; c < nchunks; c += kNB) {
+  // With preloaded scales the loop body covers kU = 8 chunks, so the scale words move to the
+  // front once per 8 chunks (4 words) instead of once per kNB chunks.
+  constexpr int kU = SU ? 8 : kNB;
+  static_assert(kU % kNB == 0 && (!SU || SW % (kU / 2) == 0), "whole slot rounds per body");
+  for (int c = 0; c < nchunks; c += kU) {
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) {
-      if (c + k >= nchunks) break;
+    for (int kk = 0; kk < kU; ++kk) {
+      const int k = kk % kNB;  // slot of chunk c + kk (c is a multiple of kNB)
+      if (c + kk >= nchunks) break;
       wait_chunk();
-      issue(c + k + kNB - 1, (k + kNB - 1) % kNB, bq[(k + kNB - 1) % kNB]);
-      issue_s(c + k + kNB - 1, (k + kNB - 1) % kNB);
-      multiply(k, bq[k], scales_of(k));
+      issue(c + kk + kNB - 1, (k + kNB - 1) % kNB, bq[(k + kNB - 1) % kNB]);
+      issue_s(c + kk + kNB - 1, (k + kNB - 1) % kNB);
+      multiply(k, bq[k], scales_of(kk));
     }
-    if constexpr (SU) {  // the next kNB chunks' scale words move to the front
+    if constexpr (SU) {  // the next kU chunks' scale words move to the front
 #pragma unroll
       for (int t = 0; t < NC; ++t)
 #pragma unroll
-        for (int i = 0; i + kNB / 2 < SW; ++i) {
-          sw[t][i] = sw[t][i + kNB / 2];
-          bw[t][i] = bw[t][i + kNB / 2];
+        for (int i = 0; i + kU / 2 < SW; ++i) {
+          sw[t][i] = sw[t][i + kU / 2];
+          bw[t][i] = bw[t][i + kU / 2];
         }
     }
   }

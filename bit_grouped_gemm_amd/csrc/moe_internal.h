@@ -127,44 +127,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
-// Byte n of a word as fp32 (v_cvt_f32_ubyteN: one instruction).
-#define MOE_CVT_UBYTE(N)                                                   \
-  __device__ __forceinline__ float ubyte##N(uint32_t x) {                 \
-    float r;                                                               \
-    asm("v_cvt_f32_ubyte" #N " %0, %1" : "=v"(r) : "v"(x));                \
-    return r;                                                              \
-  }
-MOE_CVT_UBYTE(0)
-MOE_CVT_UBYTE(1)
-MOE_CVT_UBYTE(2)
-MOE_CVT_UBYTE(3)
-#undef MOE_CVT_UBYTE
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// Dequantise one packed word (elements 8i..8i+7 at nibbles 0..7) with its group's scale s
-// and bias b: w_j = s * q_j + b in one fp32 FMA (exact whenever s*q+b fits fp32, e.g. for
-// b = -8s), then rounded to bf16. out[j/2] holds elements (j, j+1), low half first, which
-// is the operand order of the bf16 MFMA and dot instructions.
-__device__ __forceinline__ void dequant8(uint32_t w, float s, float b, uint32_t out[4]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // nibbles 0,2,4,6 in bytes 0..3
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 1,3,5,7 in bytes 0..3
-  out[0] = pack_bf16x2(__builtin_fmaf(s, ubyte0(lo), b), __builtin_fmaf(s, ubyte0(hi), b));
-  out[1] = pack_bf16x2(__builtin_fmaf(s, ubyte1(lo), b), __builtin_fmaf(s, ubyte1(hi), b));
-  out[2] = pack_bf16x2(__builtin_fmaf(s, ubyte2(lo), b), __builtin_fmaf(s, ubyte2(hi), b));
-  out[3] = pack_bf16x2(__builtin_fmaf(s, ubyte3(lo), b), __builtin_fmaf(s, ubyte3(hi), b));
+// Nibbles j and j + 4 of w (j = 0 after w >> 0, 1 after w >> 4, ...) as two fp16 values in one
+// word: the fp16 whose bit pattern is q (q < 16) is the subnormal q * 2^-24. The AND is written
+// as an instruction of its own so that the pair stays packed and each half is selected by the
+// widening multiply-add (op_sel) instead of being extracted nibble by nibble.
+__device__ __forceinline__ f16x2_t nibble_pair(uint32_t w) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(0x000F000Fu));
+  return __builtin_bit_cast(f16x2_t, r);
 }
 
-// The fp32 values before rounding (test export only).
+// Dequantise one packed word (elements 8i..8i+7 at nibbles 0..7) with its group's scale s
+// and bias b: w_j = s * q_j + b in one fp32 FMA, then rounded to bf16. The FMA takes q_j as the
+// fp16 subnormal q_j * 2^-24 (widened exactly by v_fma_mix_f32) and s * 2^24, so the product
+// is exactly s * q_j and the one rounding is that of fma(s, q_j, b), for every finite scale of
+// magnitude below 2^104 (s * 2^24 exact). out[j/2] holds elements (j, j+1), low half first,
+// which is the operand order of the bf16 MFMA and dot instructions.
 __device__ __forceinline__ void dequant8_f32(uint32_t w, float s, float b, float out[8]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  out[0] = __builtin_fmaf(s, ubyte0(lo), b);
-  out[1] = __builtin_fmaf(s, ubyte0(hi), b);
-  out[2] = __builtin_fmaf(s, ubyte1(lo), b);
-  out[3] = __builtin_fmaf(s, ubyte1(hi), b);
-  out[4] = __builtin_fmaf(s, ubyte2(lo), b);
-  out[5] = __builtin_fmaf(s, ubyte2(hi), b);
-  out[6] = __builtin_fmaf(s, ubyte3(lo), b);
-  out[7] = __builtin_fmaf(s, ubyte3(hi), b);
+  const float s24 = s * 16777216.0f;
+  const f16x2_t p0 = nibble_pair(w), p1 = nibble_pair(w >> 4), p2 = nibble_pair(w >> 8),
+                p3 = nibble_pair(w >> 12);
+  out[0] = __builtin_fmaf((float)p0.x, s24, b);
+  out[1] = __builtin_fmaf((float)p1.x, s24, b);
+  out[2] = __builtin_fmaf((float)p2.x, s24, b);
+  out[3] = __builtin_fmaf((float)p3.x, s24, b);
+  out[4] = __builtin_fmaf((float)p0.y, s24, b);
+  out[5] = __builtin_fmaf((float)p1.y, s24, b);
+  out[6] = __builtin_fmaf((float)p2.y, s24, b);
+  out[7] = __builtin_fmaf((float)p3.y, s24, b);
+}
+
+__device__ __forceinline__ void dequant8(uint32_t w, float s, float b, uint32_t out[4]) {
+  float f[8];
+  dequant8_f32(w, s, b, f);
+  out[0] = pack_bf16x2(f[0], f[1]);
+  out[1] = pack_bf16x2(f[2], f[3]);
+  out[2] = pack_bf16x2(f[4], f[5]);
+  out[3] = pack_bf16x2(f[6], f[7]);
 }
 
 // acc += a.lo*b.lo + a.hi*b.hi for packed bf16 pairs (products exact, fp32 sum).

@@ -61,7 +61,10 @@ typedef enum {
  *   q     [n_mat, N, Kin/8] uint32: element 8i+j of a row at bits [4j, 4j+4) of word i
  *   scale [n_mat, N, Kin/64] bf16, bias [n_mat, N, Kin/64] bf16
  *   weight(m, n, k) = scale[m, n, k/64] * q(m, n, k) + bias[m, n, k/64]
- * N is the output dimension and Kin the input dimension (rows are input-contiguous). */
+ * N is the output dimension and Kin the input dimension (rows are input-contiguous).
+ * Each weight is formed as one fp32 fused multiply-add of scale, q and bias and rounded to
+ * bf16; this holds for every finite scale of magnitude below 2^104 (larger scales are outside
+ * what the kernels compute exactly). */
 typedef struct {
   const uint32_t* q;
   const uint16_t* scale;
