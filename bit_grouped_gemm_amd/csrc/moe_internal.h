@@ -129,34 +129,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// Nibbles j and j + 4 of w (j = 0 after w >> 0, 1 after w >> 4, ...) as two fp16 values in one
-// word: the fp16 whose bit pattern is q (q < 16) is the subnormal q * 2^-24. The AND is written
-// as an instruction of its own so that the pair stays packed and each half is selected by the
-// widening multiply-add (op_sel) instead of being extracted nibble by nibble.
-__device__ __forceinline__ f16x2_t nibble_pair(uint32_t w) {
+// Two nibbles of w selected by mask m (0x000F000F: nibbles 0 and 4; 0x00F000F0: nibbles 1 and
+// 5) as two fp16 values in one word. A nibble q left in place is an fp16 subnormal: q * 2^-24
+// at bits 0-3, q * 2^-20 at bits 4-7. The AND is written as an instruction of its own so that
+// the pair stays packed and each half is selected by the widening multiply-add (op_sel)
+// instead of being extracted nibble by nibble.
+__device__ __forceinline__ f16x2_t nibble_pair(uint32_t w, uint32_t m) {
   uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(0x000F000Fu));
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
   return __builtin_bit_cast(f16x2_t, r);
 }
 
 // Dequantise one packed word (elements 8i..8i+7 at nibbles 0..7) with its group's scale s
 // and bias b: w_j = s * q_j + b in one fp32 FMA, then rounded to bf16. The FMA takes q_j as the
-// fp16 subnormal q_j * 2^-24 (widened exactly by v_fma_mix_f32) and s * 2^24, so the product
-// is exactly s * q_j and the one rounding is that of fma(s, q_j, b), for every finite scale of
-// magnitude below 2^104 (s * 2^24 exact). out[j/2] holds elements (j, j+1), low half first,
-// which is the operand order of the bf16 MFMA and dot instructions.
+// fp16 subnormal q_j * 2^-24 or q_j * 2^-20 (widened exactly by v_fma_mix_f32) and s * 2^24 or
+// s * 2^20, so the product is exactly s * q_j and the one rounding is that of fma(s, q_j, b),
+// for every finite scale of magnitude below 2^104 (s * 2^24 exact). One shift and four ANDs
+// expose the eight nibbles. out[j/2] holds elements (j, j+1), low half first, which is the
+// operand order of the bf16 MFMA and dot instructions.
 __device__ __forceinline__ void dequant8_f32(uint32_t w, float s, float b, float out[8]) {
-  const float s24 = s * 16777216.0f;
-  const f16x2_t p0 = nibble_pair(w), p1 = nibble_pair(w >> 4), p2 = nibble_pair(w >> 8),
-                p3 = nibble_pair(w >> 12);
+  const float s24 = s * 16777216.0f, s20 = s * 1048576.0f;
+  const uint32_t w8 = w >> 8;
+  const f16x2_t p0 = nibble_pair(w, 0x000F000Fu), p1 = nibble_pair(w, 0x00F000F0u),
+                p2 = nibble_pair(w8, 0x000F000Fu), p3 = nibble_pair(w8, 0x00F000F0u);
   out[0] = __builtin_fmaf((float)p0.x, s24, b);
-  out[1] = __builtin_fmaf((float)p1.x, s24, b);
+  out[1] = __builtin_fmaf((float)p1.x, s20, b);
   out[2] = __builtin_fmaf((float)p2.x, s24, b);
-  out[3] = __builtin_fmaf((float)p3.x, s24, b);
+  out[3] = __builtin_fmaf((float)p3.x, s20, b);
   out[4] = __builtin_fmaf((float)p0.y, s24, b);
-  out[5] = __builtin_fmaf((float)p1.y, s24, b);
+  out[5] = __builtin_fmaf((float)p1.y, s20, b);
   out[6] = __builtin_fmaf((float)p2.y, s24, b);
-  out[7] = __builtin_fmaf((float)p3.y, s24, b);
+  out[7] = __builtin_fmaf((float)p3.y, s20, b);
 }
 
 __device__ __forceinline__ void dequant8(uint32_t w, float s, float b, uint32_t out[4]) {
