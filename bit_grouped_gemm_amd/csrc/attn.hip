@@ -29,10 +29,11 @@
 //    (values) are requested as soon as the current ones have been used, so a workgroup keeps a
 //    chunk's rows in flight while it computes. The span's (max, sum, acc) per head is stored.
 //    The spans are sized so that a set number of workgroups covers the call.
-//  * k_attn_combine: per (sequence, query head), the spans' records are merged, rescaled by
-//    exp(max_s - max): weights first, then D/4 lanes per record with 16-byte loads over
-//    interleaved records, summed over the lanes' partial sums in a fixed order, so the output
-//    does not depend on scheduling.
+//  * k_attn_combine: per (sequence, query head, 32 of its dimensions), the spans' records are
+//    merged, rescaled by exp(max_s - max): the first accumulator rows and every span's (max,
+//    sum) are requested at once, then weights, then 8 lanes per record with 16-byte loads over
+//    interleaved records (256 records per request round), summed over the lanes' partial sums
+//    in a fixed order, so the output does not depend on scheduling.
 #include <algorithm>
 #include <cmath>
 
@@ -395,53 +396,80 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
 // exp(max_s - max) go to LDS; then lanes take 4 dimensions of a record each (D/4 lanes per
 // record, 256 / (D/4) records per step over interleaved records) and the per-slot sums are
 // added in slot order, so the result does not depend on scheduling.
-template <int D>
+template <int D, int DS>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
-  constexpr int TPR = D / 4;              // lanes per record
+  // a workgroup merges DS dimensions of one head (D / DS workgroups per head)
+  static_assert(D % DS == 0 && DS % 32 == 0, "whole 32-dimension slices");
+  constexpr int TPR = DS / 4;             // lanes per record
   constexpr int RPS = kAttnThreads / TPR; // records per step
   constexpr int UNR = 8;                  // records per lane requested together
   __shared__ float wts[kAttnMaxSpans];
   __shared__ float red[8];
-  __shared__ __attribute__((aligned(16))) float part_sum[RPS * D];
+  __shared__ __attribute__((aligned(16))) float part_sum[RPS * DS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x / (D / DS), ds0 = (blockIdx.x % (D / DS)) * DS;
+  const int b = blockIdx.y;
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int ns = (len + a.span - 1) / a.span;
-  float* o = a.out + ((size_t)b * a.Hq + h) * D;
+  float* o = a.out + ((size_t)b * a.Hq + h) * D + ds0;
   if (ns == 0) {
-    for (int i = tid; i < D; i += kAttnThreads) o[i] = 0.0f;
+    for (int i = tid; i < DS; i += kAttnThreads) o[i] = 0.0f;
     return;
   }
   const size_t rec = (size_t)(D + 4);
   const float* r = a.part + ((size_t)b * a.Hq + h) * a.nspans * rec;
+  // lane slot `sl` takes records sl, sl + RPS, ...; its first UNR records are requested before
+  // the maximum is known, so their round trip overlaps that of the (max, sum) pairs
+  const int sl = tid / TPR, d4 = (tid % TPR) * 4;
+  float4 v[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int cc = min(sl + u * RPS, ns - 1);
+    v[u] = *reinterpret_cast<const float4*>(r + cc * rec + 4 + ds0 + d4);
+  }
+  // the (max, sum) pairs of this thread's spans, read once
+  constexpr int kPer = kAttnMaxSpans / kAttnThreads;
+  static_assert(kAttnMaxSpans % kAttnThreads == 0, "whole spans per thread");
+  float mv[kPer], lv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + kAttnThreads * i;
+    mv[i] = c < ns ? r[c * rec] : -INFINITY;
+    lv[i] = c < ns ? r[c * rec + 1] : 0.0f;
+  }
   // the maximum over the spans
-  float M = -INFINITY;
-  for (int c = tid; c < ns; c += kAttnThreads) M = fmaxf(M, r[c * rec]);
+  float M = mv[0];
+#pragma unroll
+  for (int i = 1; i < kPer; ++i) M = fmaxf(M, mv[i]);
   M = wave_max_f(M);
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   // weights and the total sum
   float L = 0.0f;
-  for (int c = tid; c < ns; c += kAttnThreads) {
-    const float w = __expf(r[c * rec] - M);
-    wts[c] = w;
-    L = __builtin_fmaf(w, r[c * rec + 1], L);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + kAttnThreads * i;
+    if (c < ns) {
+      const float w = __expf(mv[i] - M);
+      wts[c] = w;
+      L = __builtin_fmaf(w, lv[i], L);
+    }
   }
   L = wave_sum(L);
   if (lane == 0) red[4 + wave] = L;
   __syncthreads();
   L = ((red[4] + red[5]) + red[6]) + red[7];
-  // weighted sum of the accumulators: lane slot `sl` takes records sl, sl + RPS, ...
-  const int sl = tid / TPR, d4 = (tid % TPR) * 4;
+  // weighted sum of the accumulators, records in increasing order per lane slot
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c = sl; c < ns; c += UNR * RPS) {
-    float4 v[UNR];
+    if (c != sl) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int cc = min(c + u * RPS, ns - 1);
-      v[u] = *reinterpret_cast<const float4*>(r + cc * rec + 4 + d4);
+      for (int u = 0; u < UNR; ++u) {
+        const int cc = min(c + u * RPS, ns - 1);
+        v[u] = *reinterpret_cast<const float4*>(r + cc * rec + 4 + ds0 + d4);
+      }
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -454,12 +482,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
       }
     }
   }
-  *reinterpret_cast<float4*>(part_sum + sl * D + d4) = acc;
+  *reinterpret_cast<float4*>(part_sum + sl * DS + d4) = acc;
   __syncthreads();
-  if (tid < D) {
+  if (tid < DS) {
     float tot = 0.0f;
 #pragma unroll
-    for (int k = 0; k < RPS; ++k) tot += part_sum[k * D + tid];
+    for (int k = 0; k < RPS; ++k) tot += part_sum[k * DS + tid];
     o[tid] = tot / L;
   }
 }
@@ -603,9 +631,21 @@ extern "C" int attn_gqa_decode(const attn_gqa_desc_t* desc, const uint16_t* q,
 #undef ATTN_SPLIT
     if (hipGetLastError() != hipSuccess) return MOE_HIP_ERROR;
   }
-  const dim3 gridc(desc->num_q_heads, batch);
-  if (D == 64) hipLaunchKernelGGL((k_attn_combine<64>), gridc, dim3(kAttnThreads), 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((k_attn_combine<128>), gridc, dim3(kAttnThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_combine<256>), gridc, dim3(kAttnThreads), 0, s, a);
+  // Whole heads per workgroup when every span's record fits one request round of its lanes
+  // (kAttnThreads / (D / 4) records per step, 8 steps); otherwise 32 dimensions per
+  // workgroup, so that a long context's records are requested by D / 32 workgroups per head,
+  // 256 records per round.
+  const bool whole = a.nspans <= 8 * kAttnThreads / (D / 4);
+  const dim3 gridc(desc->num_q_heads * (whole ? 1 : D / 32), batch);
+  if (D == 64) {
+    if (whole) hipLaunchKernelGGL((k_attn_combine<64, 64>), gridc, dim3(kAttnThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<64, 32>), gridc, dim3(kAttnThreads), 0, s, a);
+  } else if (D == 128) {
+    if (whole) hipLaunchKernelGGL((k_attn_combine<128, 128>), gridc, dim3(kAttnThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<128, 32>), gridc, dim3(kAttnThreads), 0, s, a);
+  } else {
+    if (whole) hipLaunchKernelGGL((k_attn_combine<256, 256>), gridc, dim3(kAttnThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<256, 32>), gridc, dim3(kAttnThreads), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }

@@ -49,7 +49,9 @@ def run(shape, lens, flags=0, seed=0, spare=3):
     return out.cpu().numpy().astype(np.float64), ref, (d, qd, kd, vd, td, ld, max_len, ws, out)
 
 
-CASES = [("tiny", [1, 15, 16, 17, 40]), ("tiny", [0, 3]), ("mid", [31, 32, 33, 700]),
+# ("tiny", [20000]): 157 spans of head size 64, merged in 32-dimension slices
+CASES = [("tiny", [1, 15, 16, 17, 40]), ("tiny", [0, 3]), ("tiny", [20000]),
+         ("mid", [31, 32, 33, 700]),
          ("wide", [63, 64, 65, 1500]), ("full", [1]), ("full", [4096]), ("full", [100, 2500, 64, 4097]),
          ("full", [32768]), ("full", [70001, 5, 131072, 1])]
 
