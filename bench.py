@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 N_LAYERS = 40                  # the stack, also the rotation pool of the single-layer sections
 T_PREFILL = 4096
 CHUNK = 512
@@ -509,9 +510,10 @@ def attention_section(contexts=(4096, 32768, 131072)):
 
 def delta_section():
     """The gated delta rule of the model's linear-attention layers (16 heads, 128 x 128 fp32
-    state): a decode step at batch 1 and 8, and a 512-token prefill chunk at batch 1. Calls
-    rotate over states in a pool of at least 320 MiB. Algorithmic bytes: the state read and
-    written once, plus the tokens' q, k, v, g, beta and o."""
+    state): a decode step at batch 1 and 8 (token-by-token kernel), and a 512-token prefill at
+    batch 1 (chunkwise kernels; the token-by-token kernel is timed beside it). Calls rotate over
+    states in a pool of at least 320 MiB. Algorithmic bytes: the state read and written once,
+    plus the tokens' q, k, v, g, beta and o."""
     import torch
     from bit_grouped_gemm_amd import delta_rule as DR
     import synth
@@ -533,6 +535,12 @@ def delta_section():
         o = torch.empty((B, T, Hv, dv), device="cuda")
         calls = [(lambda st=st: DR.forward(d, q, k, v, g, beta, st, st, o)) for st in pool]
         n = min(len(calls), 320 if T == 1 else 16)
+        token_st = None
+        if T > 1:
+            token_st = replay_stats(calls[:n], 3)
+            ws = DR.alloc_chunked_workspace(d, B, T)
+            calls = [(lambda st=st: DR.forward_chunked(d, q, k, v, g, beta, st, st, o, ws))
+                     for st in pool]
         st = replay_stats(calls[:n], max(2, 640 // n) if T == 1 else 3)
         nbytes = 2.0 * state_bytes + B * T * (2 * Hk * dk * 2 + Hv * dv * 2 + 2 * Hv * 4 + Hv * dv * 4)
         gbs = nbytes / (st["mean"] * 1e-3) / 1e9
@@ -541,9 +549,22 @@ def delta_section():
                                "bytes_per_call": nbytes, "achieved_gbs": gbs,
                                "hbm_frac": gbs / HBM_PEAK_GBS,
                                "traffic": measured_traffic(f"delta@b{B}_t{T}")}
+        if token_st is not None:
+            res[f"B={B},T={T}"]["path"] = "chunked (32-token chunks)"
+            res[f"B={B},T={T}"]["token_path_us"] = token_st["mean"] * 1e3
+            res[f"B={B},T={T}"]["chunked_speedup"] = token_st["mean"] / st["mean"]
+            # fp32 multiply-adds of the chunkwise form per (sequence, head, 32-token chunk): the
+            # chunk's kh.kh and qh.kh products, then per state row kh.S and qh.S, T R, P delta
+            # and the rank-32 state update
+            C = 32
+            fma = B * Hv * ((T + C - 1) // C) * (dv * (3 * C * dk + C * C) + 2 * C * C * dk)
+            tf = 2.0 * fma / (st["mean"] * 1e-3) / 1e12
+            res[f"B={B},T={T}"]["alu"] = {"flops_per_call": 2.0 * fma, "achieved_tflops": tf,
+                                          "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                                          "frac": tf / FP32_VECTOR_PEAK_TFLOPS}
         del pool
     return {"workload": "gated delta rule, 16 heads, 128 x 128 fp32 state per head; decode steps "
-                        "(T=1) and a 512-token chunk", "cases": res}
+                        "(T=1) and a 512-token prefill", "cases": res}
 
 
 def copy_section():

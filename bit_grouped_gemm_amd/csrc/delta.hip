@@ -295,14 +295,389 @@ __global__ __launch_bounds__(2 * DK) void k_delta_rule_blk(DeltaArgs a) {
   *reinterpret_cast<float4*>(a.s_out + srow + 4) = s1;
 }
 
+// ================================================================ chunked form (long T)
+// The same recurrence over chunks of kDeltaChunk = 32 tokens, as in the chunkwise form of
+// Gated Delta Networks (section 3 of Yang, Kautz and Hatamizadeh): within a chunk that starts
+// from state S0, with G_s the chunk's running sum of g (so exp(G_s - G_r) is the decay from
+// token r to token s),
+//   delta_s = beta_s (v_s - exp(G_s) S0 kh_s) - sum_{r<s} M[s,r] delta_r,
+//       M[s,r] = beta_s exp(G_s - G_r) (kh_s . kh_r), i.e. delta = (I + M)^-1 R = T R,
+//   o_t = exp(G_t) S0 qh_t + sum_{s<=t} P[t,s] delta_s,  P[t,s] = exp(G_t - G_s) (qh_t . kh_s),
+//   S   = exp(G_last) S0 + sum_s exp(G_last - G_s) delta_s kh_s^T,
+// which unrolls the per-token update exactly (fp32 rounding aside). T and P depend only on the
+// chunk's keys, queries, g and beta, so one pass computes them for all chunks at once; the
+// serial part is then one step per chunk instead of one per token.
+//  * k_delta_prep: one workgroup per (value head, chunk, sequence): normalises the chunk's
+//    keys and queries (as k_delta_rule_blk does), the running sums of g, the dot products
+//    kh_s . kh_r and qh_t . kh_s on fp32 MFMA, M and P, and T by a blocked inverse (8 x 8
+//    diagonal blocks by forward substitution, then two doubling steps); writes a record of
+//    T, P, kh, qh and the decays to the workspace. Tokens past T are zero keys and queries
+//    with beta = 0, so they add nothing.
+//  * k_delta_chunk: one workgroup per 8 state rows of a value head, two rows per wave; the
+//    rows stay in LDS. Per chunk, with the next chunk's record in flight: lanes s and s + 32
+//    form kh_s . S0_row and qh_s . S0_row for both rows over one half of the columns each
+//    (each k and q read serves two rows), then delta_s = (T R)_s and o_s for one row each (R
+//    and delta exchanged through LDS inside the wave); lane l then updates columns
+//    [l*dk/64, (l+1)*dk/64) of both rows.
+constexpr int kDeltaChunk = 32;
+constexpr int kDeltaChunkRows = 8;  // state rows per workgroup of k_delta_chunk
+
+// Record of one (sequence, value head, chunk): T [32][32] | P [32][32] | kh [32][DK] |
+// qh [32][DK] | exp(G) [32] | exp(G_last - G) [32] | beta [32] | exp(G_last), pad [32].
+template <int DK>
+constexpr int delta_rec_floats() { return 2 * kDeltaChunk * kDeltaChunk + 2 * kDeltaChunk * DK + 128; }
+constexpr int kRecT = 0, kRecP = kDeltaChunk * kDeltaChunk, kRecK = 2 * kDeltaChunk * kDeltaChunk;
+
+template <int DK>
+__global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restrict__ ws, int nchunks) {
+  constexpr int C = kDeltaChunk;
+  constexpr int KP = DK + 4;             // padded LDS row of kh / qh
+  constexpr int E = DK / 16;             // values per lane in the normalisation (16 lanes a token)
+  constexpr int RQ = kRecK + C * DK, RS = kRecK + 2 * C * DK;  // qh and scalar offsets
+  static_assert(E % 4 == 0, "whole 4-value pieces");
+  __shared__ __attribute__((aligned(16))) float kl[C * KP];
+  __shared__ __attribute__((aligned(16))) float ql[C * KP];
+  constexpr int LD = C + 1;              // LDS row of the 32 x 32 matrices
+  __shared__ float Ml[C * LD];           // M of the chunk (strictly lower triangular)
+  __shared__ float Tl[C * LD];           // (I + M)^-1, built block by block
+  __shared__ float Xl[2][C * LD];        // the dot products' second halves
+  __shared__ float Wl[16 * 16];
+  __shared__ float Gs[C], bl[C];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int i = j / (a.Hv / a.Hk);
+  const int t0 = c * C, n = min(C, a.T - t0);
+  float* rec = ws + (((size_t)b * a.Hv + j) * nchunks + c) * delta_rec_floats<DK>();
+
+  for (int e = tid; e < C * LD; e += 256) Tl[e] = 0.0f;  // the inverse is zero above its diagonal
+  // normalised keys and queries: 16 lanes per token, tokens wave*8 + 4*pass + lane/16
+  const int sc = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = wave * 8 + 4 * pass + (lane >> 4);
+    const int tt = min(t0 + t, a.T - 1);
+    const size_t base = (((size_t)b * a.T + tt) * a.Hk + i) * DK + E * sc;
+    float4 kf[E / 4], qf[E / 4];
+    float kk = 0.0f, qq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) {
+      kf[e] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(a.k + base + 4 * e));
+      qf[e] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(a.q + base + 4 * e));
+      kk += dot4(kf[e], kf[e]);
+      qq += dot4(qf[e], qf[e]);
+    }
+    kk = lane_group_sum<16>(kk);
+    qq = lane_group_sum<16>(qq);
+    const bool valid = t < n;
+    const float nk = valid ? 1.0f / sqrtf(kk + a.eps) : 0.0f;
+    const float nq = valid ? a.scale / sqrtf(qq + a.eps) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) {
+      *reinterpret_cast<float4*>(kl + t * KP + E * sc + 4 * e) =
+          make_float4(kf[e].x * nk, kf[e].y * nk, kf[e].z * nk, kf[e].w * nk);
+      *reinterpret_cast<float4*>(ql + t * KP + E * sc + 4 * e) =
+          make_float4(qf[e].x * nq, qf[e].y * nq, qf[e].z * nq, qf[e].w * nq);
+    }
+  }
+  // running sums of g over the chunk (lanes 0..31 of wave 0)
+  if (wave == 0) {
+    const bool valid = lane < n;
+    const size_t gi = ((size_t)b * a.T + t0 + (valid ? lane : 0)) * a.Hv + j;
+    float G = valid ? a.g[gi] : 0.0f;
+    const float bv = valid ? a.beta[gi] : 0.0f;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const float up = __shfl_up(G, o, 64);
+      if ((lane & 31) >= o) G += up;
+    }
+    if (lane < C) {
+      Gs[lane] = G;
+      bl[lane] = bv;
+    }
+  }
+  __syncthreads();
+  // kh_s . kh_r (waves 0, 1) and qh_s . kh_r (waves 2, 3) on v_mfma_f32_32x32x2_f32, each wave
+  // over one half of the key dimension. Lane l holds row l & 31 of both operands; of each
+  // 8-column piece it holds columns 4 * (l >> 5) .. + 3, which four MFMAs take in turn (both
+  // operands pair the same columns, so every column enters the sums once).
+  {
+    const float* A = (wave >> 1) ? ql : kl;
+    const int kh = (wave & 1) * (DK / 2), m = lane & 31, hs = lane >> 5;
+    f32x16_t acc = {};
+#pragma unroll
+    for (int p = 0; p < DK / 16; ++p) {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + m * KP + kh + 8 * p + 4 * hs);
+      const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(kl + m * KP + kh + 8 * p + 4 * hs);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], acc, 0, 0, 0);
+    }
+    // result register i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+    float* part = Xl[wave >> 1];
+    if (wave & 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[(8 * (i >> 2) + 4 * hs + (i & 3)) * LD + m] = acc[i];
+    }
+    __syncthreads();
+    if (!(wave & 1)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3), r = m;
+        const float v = acc[i] + part[s2 * LD + r];
+        const float e = r <= s2 ? __expf(Gs[s2] - Gs[r]) : 0.0f;
+        if (wave == 0) Ml[s2 * LD + r] = r < s2 ? bl[s2] * e * v : 0.0f;
+        else rec[kRecP + s2 * C + r] = e * v;
+      }
+    }
+    __syncthreads();
+  }
+  // T = (I + M)^-1, blocked: the four 8 x 8 diagonal blocks by forward substitution (lane
+  // 8b + c solves column c of block b), then [[A, 0], [B, D]]^-1 = [[A^-1, 0], [-D^-1 B A^-1,
+  // D^-1]] on pairs of 8 x 8 blocks and then on the two 16 x 16 halves.
+  if (tid < C) {
+    const int b8 = tid & ~7, c8 = tid & 7;
+    float tc[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      float acc = s2 == c8 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int r = 0; r < s2; ++r) acc = __builtin_fmaf(-Ml[(b8 + s2) * LD + b8 + r], tc[r], acc);
+      tc[s2] = acc;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) Tl[(b8 + s2) * LD + b8 + c8] = tc[s2];
+  }
+  __syncthreads();
+  const int pq = tid >> 6, i8 = (tid >> 3) & 7, j8 = tid & 7, o8 = 16 * pq;
+  if (tid < 128) {  // W = M_10 T_00 of the pair of blocks starting at row o8
+    float w = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w = __builtin_fmaf(Ml[(o8 + 8 + i8) * LD + o8 + k], Tl[(o8 + k) * LD + o8 + j8], w);
+    Wl[pq * 64 + i8 * 8 + j8] = w;
+  }
+  __syncthreads();
+  if (tid < 128) {  // T_10 = -T_11 W
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t = __builtin_fmaf(Tl[(o8 + 8 + i8) * LD + o8 + 8 + k], Wl[pq * 64 + k * 8 + j8], t);
+    Tl[(o8 + 8 + i8) * LD + o8 + j8] = -t;
+  }
+  __syncthreads();
+  const int i16 = tid >> 4, j16 = tid & 15;
+  {  // the same on the two halves of 16 rows
+    float w = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) w = __builtin_fmaf(Ml[(16 + i16) * LD + k], Tl[k * LD + j16], w);
+    Wl[i16 * 16 + j16] = w;
+  }
+  __syncthreads();
+  {
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t = __builtin_fmaf(Tl[(16 + i16) * LD + 16 + k], Wl[k * 16 + j16], t);
+    Tl[(16 + i16) * LD + j16] = -t;
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += 256) rec[kRecT + e] = Tl[(e / C) * LD + e % C];
+  // keys, queries and the decays
+  for (int q4 = tid; q4 < C * DK / 4; q4 += 256) {
+    const int s2 = q4 / (DK / 4), k4 = q4 % (DK / 4);
+    reinterpret_cast<float4*>(rec + kRecK)[q4] = *reinterpret_cast<const float4*>(kl + s2 * KP + 4 * k4);
+    reinterpret_cast<float4*>(rec + RQ)[q4] = *reinterpret_cast<const float4*>(ql + s2 * KP + 4 * k4);
+  }
+  if (tid < C) {
+    const float Gl = Gs[n - 1];
+    rec[RS + tid] = __expf(Gs[tid]);
+    rec[RS + C + tid] = tid < n ? __expf(Gl - Gs[tid]) : 0.0f;
+    rec[RS + 2 * C + tid] = bl[tid];
+    if (tid == 0) rec[RS + 3 * C] = __expf(Gl);
+  }
+}
+
+// LDS writes of one wave made visible to its own later reads, with no workgroup barrier
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void k_delta_chunk(DeltaArgs a, const float* __restrict__ ws,
+                                                     int nchunks) {
+  constexpr int C = kDeltaChunk, RW = kDeltaChunkRows;  // two state rows per wave
+  constexpr int KP = DK + 4;        // padded LDS row of kh / qh / the state
+  constexpr int CP = C + 4;         // padded LDS row of T / P
+  constexpr int RF = delta_rec_floats<DK>();
+  constexpr int RQ = kRecK + C * DK, RS = kRecK + 2 * C * DK;
+  constexpr int NF4 = RF / 4;                   // float4 pieces of a record
+  constexpr int PER = (NF4 + 255) / 256;        // pieces per thread
+  constexpr int CPL = DK / 64;                  // state columns per lane in the update
+  constexpr int HD = DK / 2;                    // columns per half of a token's dot products
+  static_assert(RW == 8 && CPL >= 1 && RW * C == 256, "two rows per wave, one v value per thread");
+  __shared__ __attribute__((aligned(16))) float Sl[RW * KP];
+  __shared__ __attribute__((aligned(16))) float kl[C * KP];
+  __shared__ __attribute__((aligned(16))) float ql[C * KP];
+  __shared__ __attribute__((aligned(16))) float Tl[C * CP];
+  __shared__ __attribute__((aligned(16))) float Pl[C * CP];
+  __shared__ __attribute__((aligned(16))) float scl[128];
+  __shared__ __attribute__((aligned(16))) float vl[RW * C];
+  __shared__ __attribute__((aligned(16))) float rbuf[RW * C];
+  __shared__ __attribute__((aligned(16))) float dbuf[RW * C];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w2 = 2 * __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave's first row
+  const int j = blockIdx.x, b = blockIdx.z, r0 = blockIdx.y * RW;
+  const int sl = lane & 31, h = lane >> 5;  // this lane's token, and half of the columns
+  const int row = w2 + h;                   // the row whose delta and o this lane forms
+
+  // the workgroup's state rows into LDS
+  for (int q4 = tid; q4 < RW * DK / 4; q4 += 256) {
+    const int rr = q4 / (DK / 4), k4 = q4 % (DK / 4);
+    const size_t src = (((size_t)b * a.Hv + j) * a.dv + r0 + rr) * DK + 4 * k4;
+    *reinterpret_cast<float4*>(Sl + rr * KP + 4 * k4) =
+        a.s_in ? *reinterpret_cast<const float4*>(a.s_in + src) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // a chunk's record and v values in registers, then into LDS
+  f32x4_t pr[PER];  // a native vector type: an array of it stays in registers
+  uint16_t pvb;     // the v value as raw bits: converted in stash, so fetch never waits
+  bool pvok;
+  auto fetch = [&](int cc) __attribute__((always_inline)) {
+    const f32x4_t* rec = reinterpret_cast<const f32x4_t*>(ws + (((size_t)b * a.Hv + j) * nchunks + cc) * RF);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q4 = tid + 256 * u;
+      pr[u] = rec[q4 < NF4 ? q4 : NF4 - 1];
+    }
+    const int rr = tid / C, t = cc * C + tid % C;
+    pvok = t < a.T;
+    pvb = a.v[(((size_t)b * a.T + (pvok ? t : a.T - 1)) * a.Hv + j) * a.dv + r0 + rr];
+  };
+  auto stash = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q4 = tid + 256 * u, f = 4 * q4;
+      if (q4 >= NF4) continue;  // only the last piece index can be past the record
+      float* dst;
+      if (f < kRecP) dst = Tl + (f / C) * CP + f % C;
+      else if (f < kRecK) dst = Pl + ((f - kRecP) / C) * CP + (f - kRecP) % C;
+      else if (f < RQ) dst = kl + ((f - kRecK) / DK) * KP + (f - kRecK) % DK;
+      else if (f < RS) dst = ql + ((f - RQ) / DK) * KP + (f - RQ) % DK;
+      else dst = scl + (f - RS);
+      *reinterpret_cast<f32x4_t*>(dst) = pr[u];
+    }
+    vl[tid] = pvok ? bf16_to_f32(pvb) : 0.0f;
+  };
+
+  fetch(0);
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int t0 = cc * C;
+    __syncthreads();  // the previous chunk is done with every LDS buffer
+    stash();
+    if (cc + 1 < nchunks) fetch(cc + 1);  // in flight while this chunk is computed
+    __syncthreads();
+    // kh_s . S0_row and qh_s . S0_row of token s = sl for both of the wave's rows over this
+    // lane's half of the columns (two partial sums each), then the other half's sums from lane ^ 32
+    float x[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, y[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    const float* kr = kl + sl * KP + h * HD;
+    const float* qr = ql + sl * KP + h * HD;
+    const float* sr = Sl + w2 * KP + h * HD;
+#pragma unroll
+    for (int k4 = 0; k4 < HD / 4; ++k4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * k4);
+      const float4 qv = *reinterpret_cast<const float4*>(qr + 4 * k4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sr + 4 * k4);
+      const float4 s1 = *reinterpret_cast<const float4*>(sr + KP + 4 * k4);
+      x[0][k4 & 1] += dot4(kv, s0);
+      x[1][k4 & 1] += dot4(kv, s1);
+      y[0][k4 & 1] += dot4(qv, s0);
+      y[1][k4 & 1] += dot4(qv, s1);
+    }
+    float xs[2], ys[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      xs[u] = x[u][0] + x[u][1];
+      ys[u] = y[u][0] + y[u][1];
+      xs[u] += __shfl_xor(xs[u], 32, 64);
+      ys[u] += __shfl_xor(ys[u], 32, 64);
+    }
+    const float xr = h ? xs[1] : xs[0], yr = h ? ys[1] : ys[0];
+    const float gam = scl[sl];
+    rbuf[row * C + sl] = scl[2 * C + sl] * (vl[row * C + sl] - gam * xr);
+    wave_lds_sync();  // R of the wave's rows is written and read by this wave only
+    // delta_s = sum_r T[s][r] R_r (T is zero above its diagonal)
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int r4 = 0; r4 < C / 4; r4 += 2) {
+      d0 += dot4(*reinterpret_cast<const float4*>(Tl + sl * CP + 4 * r4),
+                 *reinterpret_cast<const float4*>(rbuf + row * C + 4 * r4));
+      d1 += dot4(*reinterpret_cast<const float4*>(Tl + sl * CP + 4 * r4 + 4),
+                 *reinterpret_cast<const float4*>(rbuf + row * C + 4 * r4 + 4));
+    }
+    dbuf[row * C + sl] = d0 + d1;
+    wave_lds_sync();
+    // o_s = exp(G_s) qh_s . S0_row + sum_r P[s][r] delta_r
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int r4 = 0; r4 < C / 4; r4 += 2) {
+      o0 += dot4(*reinterpret_cast<const float4*>(Pl + sl * CP + 4 * r4),
+                 *reinterpret_cast<const float4*>(dbuf + row * C + 4 * r4));
+      o1 += dot4(*reinterpret_cast<const float4*>(Pl + sl * CP + 4 * r4 + 4),
+                 *reinterpret_cast<const float4*>(dbuf + row * C + 4 * r4 + 4));
+    }
+    if (t0 + sl < a.T)
+      a.o[(((size_t)b * a.T + t0 + sl) * a.Hv + j) * a.dv + r0 + row] = __builtin_fmaf(gam, yr, o0 + o1);
+    // columns [lane*CPL, (lane+1)*CPL) of both rows: S = exp(G_last) S0 + sum_s w_s kh_s, with
+    // w_s = exp(G_last - G_s) delta_s taken four tokens at a time
+    const float gl = scl[3 * C];
+    float* sp = Sl + w2 * KP + lane * CPL;
+    float acc[2][CPL];
+#pragma unroll
+    for (int c1 = 0; c1 < CPL; ++c1) {
+      acc[0][c1] = gl * sp[c1];
+      acc[1][c1] = gl * sp[KP + c1];
+    }
+    for (int s4 = 0; s4 < C / 4; ++s4) {
+      const float4 ge4 = *reinterpret_cast<const float4*>(scl + C + 4 * s4);
+      const float4 d04 = *reinterpret_cast<const float4*>(dbuf + w2 * C + 4 * s4);
+      const float4 d14 = *reinterpret_cast<const float4*>(dbuf + (w2 + 1) * C + 4 * s4);
+      const float wa[4] = {ge4.x * d04.x, ge4.y * d04.y, ge4.z * d04.z, ge4.w * d04.w};
+      const float wb[4] = {ge4.x * d14.x, ge4.y * d14.y, ge4.z * d14.z, ge4.w * d14.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* kq = kl + (4 * s4 + u) * KP + lane * CPL;
+#pragma unroll
+        for (int c1 = 0; c1 < CPL; ++c1) {
+          const float kc = kq[c1];
+          acc[0][c1] = __builtin_fmaf(wa[u], kc, acc[0][c1]);
+          acc[1][c1] = __builtin_fmaf(wb[u], kc, acc[1][c1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c1 = 0; c1 < CPL; ++c1) {
+      sp[c1] = acc[0][c1];
+      sp[KP + c1] = acc[1][c1];
+    }
+  }
+  __syncthreads();
+  for (int q4 = tid; q4 < RW * DK / 4; q4 += 256) {
+    const int rr = q4 / (DK / 4), k4 = q4 % (DK / 4);
+    const size_t dst = (((size_t)b * a.Hv + j) * a.dv + r0 + rr) * DK + 4 * k4;
+    *reinterpret_cast<float4*>(a.s_out + dst) = *reinterpret_cast<const float4*>(Sl + rr * KP + 4 * k4);
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
 
-extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t* q,
-                                  const uint16_t* k, const uint16_t* v, const float* g,
-                                  const float* beta, const float* state_in, float* state_out,
-                                  float* o, int32_t batch, int32_t T, void* stream) {
+namespace {
+
+// Checks shared by both entry points; T = 0 passes the state through. Returns MOE_OK with
+// *done = false when the caller should launch its kernels.
+int delta_prologue(const delta_rule_desc_t* desc, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const float* g, const float* beta, const float* state_in,
+                   float* state_out, float* o, int32_t batch, int32_t T, hipStream_t s, bool* done) {
+  *done = true;
   if (!desc) return MOE_INVALID_ARG;
   const int Hk = desc->num_k_heads, Hv = desc->num_v_heads, dk = desc->dk, dv = desc->dv;
   if (Hk <= 0 || Hv <= 0 || dv <= 0) return MOE_INVALID_ARG;
@@ -314,7 +689,6 @@ extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t*
     return MOE_INVALID_ARG;
   if (T > 0 && (!q || !k || !v || !g || !beta || !o || ((uintptr_t)q & 15) || ((uintptr_t)k & 15)))
     return MOE_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {  // no token: the state passes through (a zero state if none is given)
     const size_t n = (size_t)batch * Hv * dv * dk;
     if (state_in == state_out) return MOE_OK;
@@ -323,6 +697,27 @@ extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t*
                  ? MOE_OK : MOE_HIP_ERROR;
     return launch_fill_zero(state_out, n, s) == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
   }
+  *done = false;
+  return MOE_OK;
+}
+
+size_t delta_rec_bytes(int dk) {
+  const int rf = dk == 64 ? delta_rec_floats<64>() : dk == 128 ? delta_rec_floats<128>()
+                                                               : delta_rec_floats<256>();
+  return (size_t)rf * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t* q,
+                                  const uint16_t* k, const uint16_t* v, const float* g,
+                                  const float* beta, const float* state_in, float* state_out,
+                                  float* o, int32_t batch, int32_t T, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool done;
+  const int st = delta_prologue(desc, q, k, v, g, beta, state_in, state_out, o, batch, T, s, &done);
+  if (done) return st;
+  const int Hk = desc->num_k_heads, Hv = desc->num_v_heads, dk = desc->dk, dv = desc->dv;
   DeltaArgs a{q, k, v, g, beta, state_in, state_out, o, Hk, Hv, dv, T, desc->scale, desc->eps};
   if (T < kDeltaBlockFrom) {
     const int rpg = 4 * (64 / (dk / 4));
@@ -335,6 +730,44 @@ extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t*
     if (dk == 64) hipLaunchKernelGGL((k_delta_rule_blk<64>), grid, dim3(128), 0, s, a);
     else if (dk == 128) hipLaunchKernelGGL((k_delta_rule_blk<128>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_delta_rule_blk<256>), grid, dim3(512), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
+}
+
+extern "C" size_t delta_rule_chunked_workspace_bytes(const delta_rule_desc_t* desc,
+                                                     int32_t batch, int32_t T) {
+  if (!desc || batch <= 0 || T <= 0 || desc->num_v_heads <= 0) return 0;
+  const int dk = desc->dk;
+  if (dk != 64 && dk != 128 && dk != 256) return 0;
+  const size_t nch = ((size_t)T + kDeltaChunk - 1) / kDeltaChunk;
+  return (size_t)batch * desc->num_v_heads * nch * delta_rec_bytes(dk);
+}
+
+extern "C" int delta_rule_forward_chunked(const delta_rule_desc_t* desc, const uint16_t* q,
+                                          const uint16_t* k, const uint16_t* v, const float* g,
+                                          const float* beta, const float* state_in,
+                                          float* state_out, float* o, int32_t batch, int32_t T,
+                                          void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool done;
+  const int st = delta_prologue(desc, q, k, v, g, beta, state_in, state_out, o, batch, T, s, &done);
+  if (done) return st;
+  if (!workspace || ((uintptr_t)workspace & 15)) return MOE_INVALID_ARG;
+  if (ws_bytes < delta_rule_chunked_workspace_bytes(desc, batch, T)) return MOE_WORKSPACE_TOO_SMALL;
+  const int Hk = desc->num_k_heads, Hv = desc->num_v_heads, dk = desc->dk, dv = desc->dv;
+  DeltaArgs a{q, k, v, g, beta, state_in, state_out, o, Hk, Hv, dv, T, desc->scale, desc->eps};
+  float* ws = static_cast<float*>(workspace);
+  const int nch = (T + kDeltaChunk - 1) / kDeltaChunk;
+  const dim3 gp(Hv, nch, batch), gm(Hv, dv / kDeltaChunkRows, batch);
+  if (dk == 64) {
+    hipLaunchKernelGGL((k_delta_prep<64>), gp, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<64>), gm, dim3(256), 0, s, a, ws, nch);
+  } else if (dk == 128) {
+    hipLaunchKernelGGL((k_delta_prep<128>), gp, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<128>), gm, dim3(256), 0, s, a, ws, nch);
+  } else {
+    hipLaunchKernelGGL((k_delta_prep<256>), gp, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<256>), gm, dim3(256), 0, s, a, ws, nch);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }

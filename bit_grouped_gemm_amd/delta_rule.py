@@ -10,7 +10,7 @@ import math
 
 from .moe_w4 import _check, _p, _stream, lib
 
-EXPORTS = ("delta_rule_forward",)
+EXPORTS = ("delta_rule_forward", "delta_rule_chunked_workspace_bytes", "delta_rule_forward_chunked")
 
 
 class DeltaDesc(ctypes.Structure):
@@ -31,6 +31,11 @@ def _lib():
         L.delta_rule_forward.restype = ctypes.c_int
         L.delta_rule_forward.argtypes = [ctypes.POINTER(DeltaDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                          i32, i32, vp]
+        L.delta_rule_chunked_workspace_bytes.restype = ctypes.c_size_t
+        L.delta_rule_chunked_workspace_bytes.argtypes = [ctypes.POINTER(DeltaDesc), i32, i32]
+        L.delta_rule_forward_chunked.restype = ctypes.c_int
+        L.delta_rule_forward_chunked.argtypes = [ctypes.POINTER(DeltaDesc), vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, i32, i32, vp, ctypes.c_size_t, vp]
         L._delta_types = True
     return L
 
@@ -42,3 +47,22 @@ def forward(d: DeltaDesc, q, k, v, g, beta, state_in, state_out, o, stream=None)
     _check(_lib().delta_rule_forward(ctypes.byref(d), _p(q), _p(k), _p(v), _p(g), _p(beta),
                                      _p(state_in), _p(state_out), _p(o), B, T, _stream(stream)),
            "delta_rule_forward")
+
+
+def chunked_workspace_bytes(d: DeltaDesc, batch: int, T: int) -> int:
+    return int(_lib().delta_rule_chunked_workspace_bytes(ctypes.byref(d), batch, T))
+
+
+def alloc_chunked_workspace(d: DeltaDesc, batch: int, T: int, device="cuda"):
+    import torch
+    return torch.empty(max(16, chunked_workspace_bytes(d, batch, T)), dtype=torch.uint8, device=device)
+
+
+def forward_chunked(d: DeltaDesc, q, k, v, g, beta, state_in, state_out, o, workspace, stream=None):
+    """As forward(), over 32-token chunks, with a workspace from alloc_chunked_workspace."""
+    B, T = q.shape[0], q.shape[1]
+    _check(_lib().delta_rule_forward_chunked(ctypes.byref(d), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                             _p(state_in), _p(state_out), _p(o), B, T,
+                                             _p(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream)),
+           "delta_rule_forward_chunked")

@@ -52,6 +52,23 @@ int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t* q, const u
                        const float* state_in, float* state_out, float* o, int32_t batch,
                        int32_t T, void* stream);
 
+/* The same computation as delta_rule_forward (the same outputs up to fp32 rounding), over chunks
+ * of 32 tokens: the chunkwise form of the gated delta rule (Yang, Kautz and Hatamizadeh,
+ * section 3), in which each chunk's (I + M)^-1 and output-mixing matrix are formed for all
+ * chunks at once and the state advances one chunk per step. For long T (prefill).
+ *   workspace  device buffer of at least delta_rule_chunked_workspace_bytes(desc, batch, T)
+ *              bytes, 16-byte aligned; its contents on entry do not matter and are overwritten
+ *              (per (sequence, value head, chunk): the chunk's matrices, normalised keys and
+ *              queries and decays). Calls that share a workspace must not overlap.
+ * Returns MOE_WORKSPACE_TOO_SMALL when ws_bytes is below the size needed, else as
+ * delta_rule_forward. */
+size_t delta_rule_chunked_workspace_bytes(const delta_rule_desc_t* desc, int32_t batch, int32_t T);
+int delta_rule_forward_chunked(const delta_rule_desc_t* desc, const uint16_t* q,
+                               const uint16_t* k, const uint16_t* v, const float* g,
+                               const float* beta, const float* state_in, float* state_out,
+                               float* o, int32_t batch, int32_t T, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,6 +81,29 @@ def test_delta_rule_rejections():
                                 FAKE, 1, 1, None) == M.MOE_INVALID_ARG   # misaligned q
 
 
+def test_delta_rule_chunked_sizes_and_rejections():
+    """Workspace sizes of the chunked entry point and the argument checks that return before
+    any launch."""
+    from bit_grouped_gemm_amd import delta_rule as DR
+    L = DR._lib()
+    ok = DR.desc(16, 16, 128, 128)
+    # 16 chunks of 32 tokens x 16 heads, each record T and P (2 x 32 x 32), kh and qh
+    # (2 x 32 x 128) and 128 scalars, fp32
+    assert DR.chunked_workspace_bytes(ok, 1, 512) == 16 * 16 * (2048 + 8192 + 128) * 4
+    assert DR.chunked_workspace_bytes(ok, 2, 33) == 2 * 16 * 2 * (2048 + 8192 + 128) * 4
+    assert DR.chunked_workspace_bytes(ok, 1, 0) == 0
+    assert DR.chunked_workspace_bytes(DR.desc(16, 16, 96, 128), 1, 64) == 0
+    call = lambda d, B=1, T=64, ws=FAKE, n=1 << 30: L.delta_rule_forward_chunked(  # noqa: E731
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, T, ws, n, None)
+    for bad in (DR.desc(16, 16, 96, 128), DR.desc(16, 24, 128, 128), DR.desc(16, 16, 128, 120)):
+        assert call(bad) == M.MOE_UNSUPPORTED
+    assert call(ok, T=-1) == M.MOE_INVALID_ARG
+    assert call(ok, B=0) == M.MOE_OK
+    assert call(ok, ws=None) == M.MOE_INVALID_ARG
+    assert call(ok, ws=FAKE + 8) == M.MOE_INVALID_ARG
+    assert call(ok, n=DR.chunked_workspace_bytes(ok, 1, 64) - 1) == M.MOE_WORKSPACE_TOO_SMALL
+
+
 def test_header_declares_the_five_layer_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_permute", "moe_grouped_gemm_w4", "moe_combine", "moe_layer_forward"):
