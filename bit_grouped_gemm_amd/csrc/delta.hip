@@ -313,14 +313,15 @@ __global__ __launch_bounds__(2 * DK) void k_delta_rule_blk(DeltaArgs a) {
 //    diagonal blocks by forward substitution, then two doubling steps); writes a record of
 //    T, P, kh, qh and the decays to the workspace. Tokens past T are zero keys and queries
 //    with beta = 0, so they add nothing.
-//  * k_delta_chunk: one workgroup per 8 state rows of a value head, two rows per wave; the
-//    rows stay in LDS. Per chunk, with the next chunk's record in flight: lanes s and s + 32
-//    form kh_s . S0_row and qh_s . S0_row for both rows over one half of the columns each
-//    (each k and q read serves two rows), then delta_s = (T R)_s and o_s for one row each (R
-//    and delta exchanged through LDS inside the wave); lane l then updates columns
-//    [l*dk/64, (l+1)*dk/64) of both rows.
+//  * k_delta_chunk: one workgroup per 16 state rows of a value head, dk/16 waves (at most 8);
+//    the state stays in registers for the whole call, wave w holding columns
+//    [w*dk/NW, (w+1)*dk/NW) of the 16 rows in the accumulator layout of
+//    v_mfma_f32_16x16x4_f32. Per chunk, with the next chunk's record in flight: kh . S0 and
+//    qh . S0 on MFMA over each wave's columns (the state registers are the B operand as they
+//    are), the waves' shares added through LDS, R, delta = T R and o on VALU (one token and
+//    row per thread), then the rank-32 state update on MFMA into the same registers.
 constexpr int kDeltaChunk = 32;
-constexpr int kDeltaChunkRows = 8;  // state rows per workgroup of k_delta_chunk
+constexpr int kDeltaChunkRows = 16;  // state rows per workgroup of k_delta_chunk
 
 // Record of one (sequence, value head, chunk): T [32][32] | P [32][32] | kh [32][DK] |
 // qh [32][DK] | exp(G) [32] | exp(G_last - G) [32] | beta [32] | exp(G_last), pad [32].
@@ -494,68 +495,71 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
   }
 }
 
-// LDS writes of one wave made visible to its own later reads, with no workgroup barrier
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+template <int DK>
+constexpr int delta_chunk_waves() { return DK / 16 < 8 ? DK / 16 : 8; }
 
 template <int DK>
-__global__ __launch_bounds__(256) void k_delta_chunk(DeltaArgs a, const float* __restrict__ ws,
-                                                     int nchunks) {
-  constexpr int C = kDeltaChunk, RW = kDeltaChunkRows;  // two state rows per wave
-  constexpr int KP = DK + 4;        // padded LDS row of kh / qh / the state
-  constexpr int CP = C + 4;         // padded LDS row of T / P
+__global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(DeltaArgs a, const float* __restrict__ ws,
+                                                                             int nchunks) {
+  constexpr int C = kDeltaChunk, RW = kDeltaChunkRows;
+  constexpr int NW = delta_chunk_waves<DK>();   // wave w owns state columns [w*DK/NW, (w+1)*DK/NW)
+  constexpr int NTH = 64 * NW;
+  constexpr int NTL = DK / 16 / NW;             // 16-column state tiles per wave
+  constexpr int KP = DK + 4;                    // padded LDS row of kh / qh
+  constexpr int CP = C + 4;                     // padded LDS row of T / P and of the [row][token] buffers
   constexpr int RF = delta_rec_floats<DK>();
   constexpr int RQ = kRecK + C * DK, RS = kRecK + 2 * C * DK;
   constexpr int NF4 = RF / 4;                   // float4 pieces of a record
-  constexpr int PER = (NF4 + 255) / 256;        // pieces per thread
-  constexpr int CPL = DK / 64;                  // state columns per lane in the update
-  constexpr int HD = DK / 2;                    // columns per half of a token's dot products
-  static_assert(RW == 8 && CPL >= 1 && RW * C == 256, "two rows per wave, one v value per thread");
-  __shared__ __attribute__((aligned(16))) float Sl[RW * KP];
+  constexpr int PER = (NF4 + NTH - 1) / NTH;    // pieces per thread
+  constexpr int NPR = RW * C / NTH;             // (token, row) pairs per thread
+  static_assert(RW == 16 && NTL >= 1 && NPR >= 1 && RW * C % NTH == 0, "16 rows, whole tiles");
   __shared__ __attribute__((aligned(16))) float kl[C * KP];
   __shared__ __attribute__((aligned(16))) float ql[C * KP];
   __shared__ __attribute__((aligned(16))) float Tl[C * CP];
   __shared__ __attribute__((aligned(16))) float Pl[C * CP];
   __shared__ __attribute__((aligned(16))) float scl[128];
-  __shared__ __attribute__((aligned(16))) float vl[RW * C];
-  __shared__ __attribute__((aligned(16))) float rbuf[RW * C];
-  __shared__ __attribute__((aligned(16))) float dbuf[RW * C];
+  __shared__ float part[NW][2][C * RW];  // each wave's share of X and Y, [token][row]
+  __shared__ float vl[C * RW];           // v, [token][row]
+  __shared__ __attribute__((aligned(16))) float Rt[RW * CP];  // R, [row][token]
+  __shared__ __attribute__((aligned(16))) float Dt[RW * CP];  // delta, [row][token]
+  __shared__ float Wt[RW * CP];          // exp(G_last - G_s) delta, [row][token]
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w2 = 2 * __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave's first row
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = blockIdx.x, b = blockIdx.z, r0 = blockIdx.y * RW;
-  const int sl = lane & 31, h = lane >> 5;  // this lane's token, and half of the columns
-  const int row = w2 + h;                   // the row whose delta and o this lane forms
+  const int m16 = lane & 15, q4 = lane >> 4;
 
-  // the workgroup's state rows into LDS
-  for (int q4 = tid; q4 < RW * DK / 4; q4 += 256) {
-    const int rr = q4 / (DK / 4), k4 = q4 % (DK / 4);
-    const size_t src = (((size_t)b * a.Hv + j) * a.dv + r0 + rr) * DK + 4 * k4;
-    *reinterpret_cast<float4*>(Sl + rr * KP + 4 * k4) =
-        a.s_in ? *reinterpret_cast<const float4*>(a.s_in + src) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // The state in the accumulator layout of v_mfma_f32_16x16x4_f32, as S^T tiles [column][row]:
+  // register i of lane l in tile u holds S[r0 + l % 16][c0 + 4 (l / 16) + i], c0 = 16 (w NTL + u).
+  f32x4_t st[NTL];
+#pragma unroll
+  for (int u = 0; u < NTL; ++u) {
+    const int c0 = 16 * (wave * NTL + u);
+    const size_t src = (((size_t)b * a.Hv + j) * a.dv + r0 + m16) * DK + c0 + 4 * q4;
+    st[u] = a.s_in ? *reinterpret_cast<const f32x4_t*>(a.s_in + src) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   // a chunk's record and v values in registers, then into LDS
   f32x4_t pr[PER];  // a native vector type: an array of it stays in registers
-  uint16_t pvb;     // the v value as raw bits: converted in stash, so fetch never waits
-  bool pvok;
+  uint16_t pvb[NPR];  // v as raw bits: converted in stash, so fetch never waits
+  bool pvok[NPR];
   auto fetch = [&](int cc) __attribute__((always_inline)) {
     const f32x4_t* rec = reinterpret_cast<const f32x4_t*>(ws + (((size_t)b * a.Hv + j) * nchunks + cc) * RF);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q4 = tid + 256 * u;
-      pr[u] = rec[q4 < NF4 ? q4 : NF4 - 1];
+      const int q = tid + NTH * u;
+      pr[u] = rec[q < NF4 ? q : NF4 - 1];
     }
-    const int rr = tid / C, t = cc * C + tid % C;
-    pvok = t < a.T;
-    pvb = a.v[(((size_t)b * a.T + (pvok ? t : a.T - 1)) * a.Hv + j) * a.dv + r0 + rr];
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) {
+      const int p = tid + NTH * e, t = cc * C + p / RW;
+      pvok[e] = t < a.T;
+      pvb[e] = a.v[(((size_t)b * a.T + (pvok[e] ? t : a.T - 1)) * a.Hv + j) * a.dv + r0 + p % RW];
+    }
   };
   auto stash = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q4 = tid + 256 * u, f = 4 * q4;
-      if (q4 >= NF4) continue;  // only the last piece index can be past the record
+      const int q = tid + NTH * u, f = 4 * q;
+      if (q >= NF4) continue;  // only the last piece index can be past the record
       float* dst;
       if (f < kRecP) dst = Tl + (f / C) * CP + f % C;
       else if (f < kRecK) dst = Pl + ((f - kRecP) / C) * CP + (f - kRecP) % C;
@@ -564,7 +568,8 @@ __global__ __launch_bounds__(256) void k_delta_chunk(DeltaArgs a, const float* _
       else dst = scl + (f - RS);
       *reinterpret_cast<f32x4_t*>(dst) = pr[u];
     }
-    vl[tid] = pvok ? bf16_to_f32(pvb) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) vl[tid + NTH * e] = pvok[e] ? bf16_to_f32(pvb[e]) : 0.0f;
   };
 
   fetch(0);
@@ -574,95 +579,100 @@ __global__ __launch_bounds__(256) void k_delta_chunk(DeltaArgs a, const float* _
     stash();
     if (cc + 1 < nchunks) fetch(cc + 1);  // in flight while this chunk is computed
     __syncthreads();
-    // kh_s . S0_row and qh_s . S0_row of token s = sl for both of the wave's rows over this
-    // lane's half of the columns (two partial sums each), then the other half's sums from lane ^ 32
-    float x[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, y[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    const float* kr = kl + sl * KP + h * HD;
-    const float* qr = ql + sl * KP + h * HD;
-    const float* sr = Sl + w2 * KP + h * HD;
+    // X[s][r] = kh_s . S0_r and Y[s][r] = qh_s . S0_r over this wave's columns, two 16-token
+    // tiles each: A = kh or qh [token][column], B = the state tile; lanes l / 16 = 0..3 supply
+    // columns c0 + 4 (l / 16) + i in step i, the same columns their state registers hold
+    f32x4_t ax[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4_t ay[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k4 = 0; k4 < HD / 4; ++k4) {
-      const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * k4);
-      const float4 qv = *reinterpret_cast<const float4*>(qr + 4 * k4);
-      const float4 s0 = *reinterpret_cast<const float4*>(sr + 4 * k4);
-      const float4 s1 = *reinterpret_cast<const float4*>(sr + KP + 4 * k4);
-      x[0][k4 & 1] += dot4(kv, s0);
-      x[1][k4 & 1] += dot4(kv, s1);
-      y[0][k4 & 1] += dot4(qv, s0);
-      y[1][k4 & 1] += dot4(qv, s1);
-    }
-    float xs[2], ys[2];
+    for (int u = 0; u < NTL; ++u) {
+      const int c0 = 16 * (wave * NTL + u);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      xs[u] = x[u][0] + x[u][1];
-      ys[u] = y[u][0] + y[u][1];
-      xs[u] += __shfl_xor(xs[u], 32, 64);
-      ys[u] += __shfl_xor(ys[u], 32, 64);
-    }
-    const float xr = h ? xs[1] : xs[0], yr = h ? ys[1] : ys[0];
-    const float gam = scl[sl];
-    rbuf[row * C + sl] = scl[2 * C + sl] * (vl[row * C + sl] - gam * xr);
-    wave_lds_sync();  // R of the wave's rows is written and read by this wave only
-    // delta_s = sum_r T[s][r] R_r (T is zero above its diagonal)
-    float d0 = 0.0f, d1 = 0.0f;
+      for (int h = 0; h < 2; ++h) {
+        const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kl + (16 * h + m16) * KP + c0 + 4 * q4);
+        const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(ql + (16 * h + m16) * KP + c0 + 4 * q4);
 #pragma unroll
-    for (int r4 = 0; r4 < C / 4; r4 += 2) {
-      d0 += dot4(*reinterpret_cast<const float4*>(Tl + sl * CP + 4 * r4),
-                 *reinterpret_cast<const float4*>(rbuf + row * C + 4 * r4));
-      d1 += dot4(*reinterpret_cast<const float4*>(Tl + sl * CP + 4 * r4 + 4),
-                 *reinterpret_cast<const float4*>(rbuf + row * C + 4 * r4 + 4));
-    }
-    dbuf[row * C + sl] = d0 + d1;
-    wave_lds_sync();
-    // o_s = exp(G_s) qh_s . S0_row + sum_r P[s][r] delta_r
-    float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-    for (int r4 = 0; r4 < C / 4; r4 += 2) {
-      o0 += dot4(*reinterpret_cast<const float4*>(Pl + sl * CP + 4 * r4),
-                 *reinterpret_cast<const float4*>(dbuf + row * C + 4 * r4));
-      o1 += dot4(*reinterpret_cast<const float4*>(Pl + sl * CP + 4 * r4 + 4),
-                 *reinterpret_cast<const float4*>(dbuf + row * C + 4 * r4 + 4));
-    }
-    if (t0 + sl < a.T)
-      a.o[(((size_t)b * a.T + t0 + sl) * a.Hv + j) * a.dv + r0 + row] = __builtin_fmaf(gam, yr, o0 + o1);
-    // columns [lane*CPL, (lane+1)*CPL) of both rows: S = exp(G_last) S0 + sum_s w_s kh_s, with
-    // w_s = exp(G_last - G_s) delta_s taken four tokens at a time
-    const float gl = scl[3 * C];
-    float* sp = Sl + w2 * KP + lane * CPL;
-    float acc[2][CPL];
-#pragma unroll
-    for (int c1 = 0; c1 < CPL; ++c1) {
-      acc[0][c1] = gl * sp[c1];
-      acc[1][c1] = gl * sp[KP + c1];
-    }
-    for (int s4 = 0; s4 < C / 4; ++s4) {
-      const float4 ge4 = *reinterpret_cast<const float4*>(scl + C + 4 * s4);
-      const float4 d04 = *reinterpret_cast<const float4*>(dbuf + w2 * C + 4 * s4);
-      const float4 d14 = *reinterpret_cast<const float4*>(dbuf + (w2 + 1) * C + 4 * s4);
-      const float wa[4] = {ge4.x * d04.x, ge4.y * d04.y, ge4.z * d04.z, ge4.w * d04.w};
-      const float wb[4] = {ge4.x * d14.x, ge4.y * d14.y, ge4.z * d14.z, ge4.w * d14.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* kq = kl + (4 * s4 + u) * KP + lane * CPL;
-#pragma unroll
-        for (int c1 = 0; c1 < CPL; ++c1) {
-          const float kc = kq[c1];
-          acc[0][c1] = __builtin_fmaf(wa[u], kc, acc[0][c1]);
-          acc[1][c1] = __builtin_fmaf(wb[u], kc, acc[1][c1]);
+        for (int i = 0; i < 4; ++i) {
+          ax[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], st[u][i], ax[h], 0, 0, 0);
+          ay[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[i], st[u][i], ay[h], 0, 0, 0);
         }
       }
     }
+    // result register i of lane l: token 16 h + 4 (l / 16) + i, row l % 16
 #pragma unroll
-    for (int c1 = 0; c1 < CPL; ++c1) {
-      sp[c1] = acc[0][c1];
-      sp[KP + c1] = acc[1][c1];
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part[wave][0][(16 * h + 4 * q4 + i) * RW + m16] = ax[h][i];
+        part[wave][1][(16 * h + 4 * q4 + i) * RW + m16] = ay[h][i];
+      }
+    }
+    __syncthreads();
+    // the waves' shares added; R = beta (v - exp(G) X) stored [row][token]; exp(G) Y kept
+    float gy[NPR];
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) {
+      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
+      float x = 0.0f, y = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        x += part[w][0][p];
+        y += part[w][1][p];
+      }
+      gy[e] = scl[s2] * y;
+      Rt[r * CP + s2] = scl[2 * C + s2] * (vl[p] - scl[s2] * x);
+    }
+    __syncthreads();
+    // delta_s = sum_r T[s][r] R_r (T is zero above its diagonal), and the update weights
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) {
+      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
+      float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < C / 4; k4 += 2) {
+        d0 += dot4(*reinterpret_cast<const float4*>(Tl + s2 * CP + 4 * k4),
+                   *reinterpret_cast<const float4*>(Rt + r * CP + 4 * k4));
+        d1 += dot4(*reinterpret_cast<const float4*>(Tl + s2 * CP + 4 * k4 + 4),
+                   *reinterpret_cast<const float4*>(Rt + r * CP + 4 * k4 + 4));
+      }
+      Dt[r * CP + s2] = d0 + d1;
+      Wt[r * CP + s2] = scl[C + s2] * (d0 + d1);
+    }
+    __syncthreads();
+    // o_s = exp(G_s) qh_s . S0 + sum_r P[s][r] delta_r
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) {
+      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
+      float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < C / 4; k4 += 2) {
+        o0 += dot4(*reinterpret_cast<const float4*>(Pl + s2 * CP + 4 * k4),
+                   *reinterpret_cast<const float4*>(Dt + r * CP + 4 * k4));
+        o1 += dot4(*reinterpret_cast<const float4*>(Pl + s2 * CP + 4 * k4 + 4),
+                   *reinterpret_cast<const float4*>(Dt + r * CP + 4 * k4 + 4));
+      }
+      if (t0 + s2 < a.T)
+        a.o[(((size_t)b * a.T + t0 + s2) * a.Hv + j) * a.dv + r0 + r] = gy[e] + (o0 + o1);
+    }
+    // S^T = exp(G_last) S0^T + kh^T W on the state tiles: A = kh [column][token], B = W
+    // [token][row]; lanes l / 16 = 0..3 supply token 4 k + l / 16 in step k
+    const float gl = scl[3 * C];
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+      const int c0 = 16 * (wave * NTL + u);
+      st[u] *= gl;
+#pragma unroll
+      for (int k = 0; k < C / 4; ++k) {
+        const int s2 = 4 * k + q4;
+        st[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kl[s2 * KP + c0 + m16], Wt[m16 * CP + s2], st[u], 0, 0, 0);
+      }
     }
   }
-  __syncthreads();
-  for (int q4 = tid; q4 < RW * DK / 4; q4 += 256) {
-    const int rr = q4 / (DK / 4), k4 = q4 % (DK / 4);
-    const size_t dst = (((size_t)b * a.Hv + j) * a.dv + r0 + rr) * DK + 4 * k4;
-    *reinterpret_cast<float4*>(a.s_out + dst) = *reinterpret_cast<const float4*>(Sl + rr * KP + 4 * k4);
+#pragma unroll
+  for (int u = 0; u < NTL; ++u) {
+    const int c0 = 16 * (wave * NTL + u);
+    const size_t dst = (((size_t)b * a.Hv + j) * a.dv + r0 + m16) * DK + c0 + 4 * q4;
+    *reinterpret_cast<f32x4_t*>(a.s_out + dst) = st[u];
   }
 }
 
@@ -761,13 +771,13 @@ extern "C" int delta_rule_forward_chunked(const delta_rule_desc_t* desc, const u
   const dim3 gp(Hv, nch, batch), gm(Hv, dv / kDeltaChunkRows, batch);
   if (dk == 64) {
     hipLaunchKernelGGL((k_delta_prep<64>), gp, dim3(256), 0, s, a, ws, nch);
-    hipLaunchKernelGGL((k_delta_chunk<64>), gm, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<64>), gm, dim3(64 * delta_chunk_waves<64>()), 0, s, a, ws, nch);
   } else if (dk == 128) {
     hipLaunchKernelGGL((k_delta_prep<128>), gp, dim3(256), 0, s, a, ws, nch);
-    hipLaunchKernelGGL((k_delta_chunk<128>), gm, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<128>), gm, dim3(64 * delta_chunk_waves<128>()), 0, s, a, ws, nch);
   } else {
     hipLaunchKernelGGL((k_delta_prep<256>), gp, dim3(256), 0, s, a, ws, nch);
-    hipLaunchKernelGGL((k_delta_chunk<256>), gm, dim3(256), 0, s, a, ws, nch);
+    hipLaunchKernelGGL((k_delta_chunk<256>), gm, dim3(64 * delta_chunk_waves<256>()), 0, s, a, ws, nch);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_HIP_ERROR;
 }
