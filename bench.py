@@ -552,6 +552,8 @@ def delta_section():
         if token_st is not None:
             res[f"B={B},T={T}"]["path"] = "chunked (32-token chunks)"
             res[f"B={B},T={T}"]["token_path_us"] = token_st["mean"] * 1e3
+            # HBM bytes per launch of the prep kernel ("traffic" is the main kernel's)
+            res[f"B={B},T={T}"]["prep_traffic"] = measured_traffic(f"delta_prep@b{B}_t{T}")
             res[f"B={B},T={T}"]["chunked_speedup"] = token_st["mean"] / st["mean"]
             # fp32 multiply-adds of the chunkwise form per (sequence, head, 32-token chunk): the
             # chunk's kh.kh and qh.kh products, then per state row kh.S and qh.S, T R, P delta
