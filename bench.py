@@ -771,7 +771,11 @@ def main():
         f"({greedy['hbm_frac'] * 100:.1f} % of HBM)")
     delta = delta_section()
     for k_, r_ in delta["cases"].items():
-        log(f"delta rule {k_}: {r_['us_per_call']:.2f} us ({r_['hbm_frac'] * 100:.1f} % of HBM)")
+        if "alu" in r_:
+            log(f"delta rule {k_}: {r_['us_per_call']:.2f} us chunkwise ({r_['alu']['frac'] * 100:.1f} % "
+                f"of fp32 vector peak; token by token {r_['token_path_us']:.1f} us)")
+        else:
+            log(f"delta rule {k_}: {r_['us_per_call']:.2f} us ({r_['hbm_frac'] * 100:.1f} % of HBM)")
     log(f"timed sections took {time.time() - t_all:.1f}s")
     cpu = None if args.skip_cpu else cpu_baseline(pool, args.cpu_seconds)
 

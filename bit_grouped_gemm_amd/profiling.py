@@ -207,6 +207,7 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--title", default="rocprofv3 kernel trace")
+    s.add_argument("--top", type=int, default=25, help="kernels listed, by total time")
     t = sub.add_parser("traffic")
     for a in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "key", "out"):
         t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
@@ -223,7 +224,7 @@ def main():
             print(k[:60], {c: round(v[1], 1) for c, v in cs.items()})
         return
     if args.action == "stats":
-        for r in write_stats_md(args.trace_dir, args.cmd, args.out, args.title)[:12]:
+        for r in write_stats_md(args.trace_dir, args.cmd, args.out, args.title, args.top)[:12]:
             print(f"{r['kernel'][:60]:60s} {r['calls']:6d} {r['avg_us']:9.2f}")
     else:
         update_traffic(args)
