@@ -350,21 +350,36 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
   const int i = j / (a.Hv / a.Hk);
   const int t0 = c * C, n = min(C, a.T - t0);
   float* rec = ws + (((size_t)b * a.Hv + j) * nchunks + c) * delta_rec_floats<DK>();
+  // g and beta of the chunk's tokens (lanes 0..31 of wave 0), requested first
+  const bool gvalid = wave == 0 && lane < n;
+  const size_t gi = ((size_t)b * a.T + t0 + (gvalid ? lane : 0)) * a.Hv + j;
+  float G = gvalid ? a.g[gi] : 0.0f;
+  const float bv = gvalid ? a.beta[gi] : 0.0f;
 
   for (int e = tid; e < C * LD; e += 256) Tl[e] = 0.0f;  // the inverse is zero above its diagonal
-  // normalised keys and queries: 16 lanes per token, tokens wave*8 + 4*pass + lane/16
+  // normalised keys and queries: 16 lanes per token, tokens wave*8 + 4*pass + lane/16; both
+  // passes' raw bf16 words are requested before any is converted
   const int sc = lane & 15;
+  uint2 kw[2][E / 4], qw[2][E / 4];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tt = min(t0 + wave * 8 + 4 * pass + (lane >> 4), a.T - 1);
+    const size_t base = (((size_t)b * a.T + tt) * a.Hk + i) * DK + E * sc;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) {
+      kw[pass][e] = *reinterpret_cast<const uint2*>(a.k + base + 4 * e);
+      qw[pass][e] = *reinterpret_cast<const uint2*>(a.q + base + 4 * e);
+    }
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int t = wave * 8 + 4 * pass + (lane >> 4);
-    const int tt = min(t0 + t, a.T - 1);
-    const size_t base = (((size_t)b * a.T + tt) * a.Hk + i) * DK + E * sc;
     float4 kf[E / 4], qf[E / 4];
     float kk = 0.0f, qq = 0.0f;
 #pragma unroll
     for (int e = 0; e < E / 4; ++e) {
-      kf[e] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(a.k + base + 4 * e));
-      qf[e] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(a.q + base + 4 * e));
+      kf[e] = bf16x4_to_f32(kw[pass][e]);
+      qf[e] = bf16x4_to_f32(qw[pass][e]);
       kk += dot4(kf[e], kf[e]);
       qq += dot4(qf[e], qf[e]);
     }
@@ -383,10 +398,6 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
   }
   // running sums of g over the chunk (lanes 0..31 of wave 0)
   if (wave == 0) {
-    const bool valid = lane < n;
-    const size_t gi = ((size_t)b * a.T + t0 + (valid ? lane : 0)) * a.Hv + j;
-    float G = valid ? a.g[gi] : 0.0f;
-    const float bv = valid ? a.beta[gi] : 0.0f;
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
       const float up = __shfl_up(G, o, 64);
@@ -420,14 +431,22 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
       for (int i = 0; i < 16; ++i) part[(8 * (i >> 2) + 4 * hs + (i & 3)) * LD + m] = acc[i];
     }
     __syncthreads();
-    if (!(wave & 1)) {
+    if (!(wave & 1)) {  // column r = m of rows s2(i); every LDS read first, then no branches
+      float pv[16], gs[16], bs[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3), r = m;
-        const float v = acc[i] + part[s2 * LD + r];
-        const float e = r <= s2 ? __expf(Gs[s2] - Gs[r]) : 0.0f;
-        if (wave == 0) Ml[s2 * LD + r] = r < s2 ? bl[s2] * e * v : 0.0f;
-        else rec[kRecP + s2 * C + r] = e * v;
+        const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
+        pv[i] = part[s2 * LD + m];
+        gs[i] = Gs[s2];
+        bs[i] = bl[s2];
+      }
+      const float gr = Gs[m];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
+        const float v = (acc[i] + pv[i]) * __expf(gs[i] - gr);  // used only where r <= s2
+        if (wave == 0) Ml[s2 * LD + m] = m < s2 ? bs[i] * v : 0.0f;
+        else rec[kRecP + s2 * C + m] = m <= s2 ? v : 0.0f;
       }
     }
     __syncthreads();
