@@ -35,6 +35,7 @@ DELTA_SHAPES = {
     "mid": DeltaShape(4, 4, 64, 64),
     "full": DeltaShape(16, 16, 128, 128),
     "gva": DeltaShape(8, 16, 128, 128),
+    "wide": DeltaShape(2, 4, 256, 48),   # the widest supported key dimension, dv not a multiple of 32
 }
 
 

@@ -55,7 +55,8 @@ def check(tag, o, s, ref_o, ref_s):
 
 @pytest.mark.parametrize("name,B,T", [("tiny", 3, 7), ("mid", 2, 33), ("full", 1, 1),
                                       ("full", 8, 1), ("full", 2, 64), ("gva", 1, 40),
-                                      ("full", 1, 256), ("full", 1, 512)])
+                                      ("full", 1, 256), ("full", 1, 512), ("wide", 3, 5),
+                                      ("wide", 2, 40)])
 def test_recurrence_matches_oracle(name, B, T):
     shape = synth.DELTA_SHAPES[name]
     log(f"[delta] start {name} B={B} T={T}")
@@ -65,7 +66,8 @@ def test_recurrence_matches_oracle(name, B, T):
 @pytest.mark.parametrize("name,B,T", [("tiny", 3, 7), ("tiny", 2, 65), ("mid", 2, 33), ("mid", 1, 96),
                                       ("full", 1, 1), ("full", 8, 1), ("full", 2, 31),
                                       ("full", 2, 32), ("full", 1, 64), ("gva", 1, 40),
-                                      ("gva", 2, 100), ("full", 1, 256), ("full", 1, 512)])
+                                      ("gva", 2, 100), ("full", 1, 256), ("full", 1, 512),
+                                      ("wide", 3, 5), ("wide", 2, 70)])
 def test_chunked_recurrence_matches_oracle(name, B, T):
     shape = synth.DELTA_SHAPES[name]
     log(f"[delta] chunked start {name} B={B} T={T}")
