@@ -299,64 +299,94 @@ __global__ __launch_bounds__(2 * DK) void k_delta_rule_blk(DeltaArgs a) {
 // The same recurrence over chunks of kDeltaChunk = 32 tokens, as in the chunkwise form of
 // Gated Delta Networks (section 3 of Yang, Kautz and Hatamizadeh): within a chunk that starts
 // from state S0, with G_s the chunk's running sum of g (so exp(G_s - G_r) is the decay from
-// token r to token s),
-//   delta_s = beta_s (v_s - exp(G_s) S0 kh_s) - sum_{r<s} M[s,r] delta_r,
+// token r to token s) and gamma_s = exp(G_s),
+//   delta_s = beta_s (v_s - gamma_s S0 kh_s) - sum_{r<s} M[s,r] delta_r,
 //       M[s,r] = beta_s exp(G_s - G_r) (kh_s . kh_r), i.e. delta = (I + M)^-1 R = T R,
-//   o_t = exp(G_t) S0 qh_t + sum_{s<=t} P[t,s] delta_s,  P[t,s] = exp(G_t - G_s) (qh_t . kh_s),
+//   o_t = gamma_t S0 qh_t + sum_{s<=t} P[t,s] delta_s,  P[t,s] = exp(G_t - G_s) (qh_t . kh_s),
 //   S   = exp(G_last) S0 + sum_s exp(G_last - G_s) delta_s kh_s^T,
-// which unrolls the per-token update exactly (fp32 rounding aside). T and P depend only on the
-// chunk's keys, queries, g and beta, so one pass computes them for all chunks at once; the
-// serial part is then one step per chunk instead of one per token.
+// which unrolls the per-token update exactly (fp32 rounding aside). Written as matrices over
+// the chunk's tokens (rows) and the state's rows (columns), with U = T diag(beta gamma) Kh,
+// Vb = T diag(beta) V, Q' = diag(gamma) Qh - P U and O' = P Vb:
+//   delta = Vb - U S0^T,   o = O' + Q' S0^T,
+// where U, Vb, Q' and O' depend only on the chunk's inputs, so one pass forms them for all
+// chunks at once and the serial part is one product with the state per chunk.
 //  * k_delta_prep: one workgroup per (value head, chunk, sequence): normalises the chunk's
 //    keys and queries (as k_delta_rule_blk does), the running sums of g, the dot products
-//    kh_s . kh_r and qh_t . kh_s on fp32 MFMA, M and P, and T by a blocked inverse (8 x 8
-//    diagonal blocks by forward substitution, then two doubling steps); writes a record of
-//    T, P, kh, qh and the decays to the workspace. Tokens past T are zero keys and queries
-//    with beta = 0, so they add nothing.
+//    kh_s . kh_r and qh_t . kh_s on fp32 MFMA, M and P, T by a blocked inverse (8 x 8
+//    diagonal blocks by forward substitution, then two doubling steps), then U, Q', Vb and O'
+//    on fp32 MFMA, 32 columns per wave at a time; writes them, kh transposed and the decays
+//    to the chunk's record. Tokens past T are zero keys and queries with beta = 0, so they
+//    add nothing.
 //  * k_delta_chunk: one workgroup per 16 state rows of a value head, dk/16 waves (at most 8);
 //    the state stays in registers for the whole call, wave w holding columns
 //    [w*dk/NW, (w+1)*dk/NW) of the 16 rows in the accumulator layout of
-//    v_mfma_f32_16x16x4_f32. Per chunk, with the next chunk's record in flight: kh . S0 and
-//    qh . S0 on MFMA over each wave's columns (the state registers are the B operand as they
-//    are), the waves' shares added through LDS, R, delta = T R and o on VALU (one token and
-//    row per thread), then the rank-32 state update on MFMA into the same registers.
+//    v_mfma_f32_16x16x4_f32. A wave loads its own columns of U, Q' and kh^T straight into
+//    registers, one chunk ahead. Per chunk: U S0^T and Q' S0^T on MFMA over each wave's
+//    columns (the state registers are the B operand as they are), the waves' shares added
+//    through LDS into delta and o, then the rank-32 state update on MFMA into the same
+//    registers: two workgroup barriers per chunk.
 constexpr int kDeltaChunk = 32;
 constexpr int kDeltaChunkRows = 16;  // state rows per workgroup of k_delta_chunk
 
-// Record of one (sequence, value head, chunk): T [32][32] | P [32][32] | kh [32][DK] |
-// qh [32][DK] | exp(G) [32] | exp(G_last - G) [32] | beta [32] | exp(G_last), pad [32].
-template <int DK>
-constexpr int delta_rec_floats() { return 2 * kDeltaChunk * kDeltaChunk + 2 * kDeltaChunk * DK + 128; }
-constexpr int kRecT = 0, kRecP = kDeltaChunk * kDeltaChunk, kRecK = 2 * kDeltaChunk * kDeltaChunk;
+// Record of one (sequence, value head, chunk), in floats: U [32][dk] | Q' [32][dk] |
+// kh^T [dk][32] | Vb [32][dv] | O' [32][dv] | exp(G_last - G_s) [32], exp(G_last), pad [31].
+__host__ __device__ constexpr size_t delta_rec_floats(int dk, int dv) {
+  return 3 * (size_t)kDeltaChunk * dk + 2 * (size_t)kDeltaChunk * dv + 64;
+}
+
+// LDS writes of one wave made visible to its own later reads, with no workgroup barrier
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int DK>
 __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restrict__ ws, int nchunks) {
   constexpr int C = kDeltaChunk;
   constexpr int KP = DK + 4;             // padded LDS row of kh / qh
   constexpr int E = DK / 16;             // values per lane in the normalisation (16 lanes a token)
-  constexpr int RQ = kRecK + C * DK, RS = kRecK + 2 * C * DK;  // qh and scalar offsets
   static_assert(E % 4 == 0, "whole 4-value pieces");
   __shared__ __attribute__((aligned(16))) float kl[C * KP];
   __shared__ __attribute__((aligned(16))) float ql[C * KP];
-  constexpr int LD = C + 1;              // LDS row of the 32 x 32 matrices
+  constexpr int LD = C + 1;              // LDS row of the 32 x 32 matrices read by columns
+  constexpr int TP = C + 4;              // LDS row of T and P, read in 16-byte pieces
   __shared__ float Ml[C * LD];           // M of the chunk (strictly lower triangular)
-  __shared__ float Tl[C * LD];           // (I + M)^-1, built block by block
+  __shared__ __attribute__((aligned(16))) float Tl[C * TP];  // (I + M)^-1, built block by block
+  __shared__ __attribute__((aligned(16))) float Pl[C * TP];  // P (lower triangular)
   __shared__ float Xl[2][C * LD];        // the dot products' second halves
+  __shared__ float Sw[4][C * LD];        // per wave: a 32 x 32 result on its way to a B operand
   __shared__ float Wl[16 * 16];
-  __shared__ float Gs[C], bl[C];
+  __shared__ float Gs[C], bl[C], gam[C], bgl[C];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int i = j / (a.Hv / a.Hk);
   const int t0 = c * C, n = min(C, a.T - t0);
-  float* rec = ws + (((size_t)b * a.Hv + j) * nchunks + c) * delta_rec_floats<DK>();
+  const int dv = a.dv;
+  float* rec = ws + (((size_t)b * a.Hv + j) * nchunks + c) * delta_rec_floats(DK, dv);
+  const size_t oQ = (size_t)C * DK, oKT = 2 * oQ, oVB = 3 * oQ, oOB = oVB + (size_t)C * dv,
+               oSC = oOB + (size_t)C * dv;
   // g and beta of the chunk's tokens (lanes 0..31 of wave 0), requested first
   const bool gvalid = wave == 0 && lane < n;
   const size_t gi = ((size_t)b * a.T + t0 + (gvalid ? lane : 0)) * a.Hv + j;
   float G = gvalid ? a.g[gi] : 0.0f;
   const float bv = gvalid ? a.beta[gi] : 0.0f;
 
-  for (int e = tid; e < C * LD; e += 256) Tl[e] = 0.0f;  // the inverse is zero above its diagonal
+  // v of this wave's first 32 state rows (lane l: row 32 w + l % 32, tokens 16 (l / 32) + jj),
+  // requested now and used after the inverse
+  const int vm = lane & 31, vhs = lane >> 5;
+  uint16_t vr[16];
+  auto load_v = [&](int vt) __attribute__((always_inline)) {
+    const int r = min(32 * vt + vm, a.dv - 1);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int t = min(t0 + 16 * vhs + jj, a.T - 1);
+      vr[jj] = a.v[(((size_t)b * a.T + t) * a.Hv + j) * a.dv + r];
+    }
+  };
+  load_v(wave);
+  for (int e = tid; e < C * TP; e += 256) Tl[e] = 0.0f;  // the inverse is zero above its diagonal
   // normalised keys and queries: 16 lanes per token, tokens wave*8 + 4*pass + lane/16; both
   // passes' raw bf16 words are requested before any is converted
   const int sc = lane & 15;
@@ -406,6 +436,8 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
     if (lane < C) {
       Gs[lane] = G;
       bl[lane] = bv;
+      gam[lane] = __expf(G);
+      bgl[lane] = bv * __expf(G);
     }
   }
   __syncthreads();
@@ -446,7 +478,7 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
         const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
         const float v = (acc[i] + pv[i]) * __expf(gs[i] - gr);  // used only where r <= s2
         if (wave == 0) Ml[s2 * LD + m] = m < s2 ? bs[i] * v : 0.0f;
-        else rec[kRecP + s2 * C + m] = m <= s2 ? v : 0.0f;
+        else Pl[s2 * TP + m] = m <= s2 ? v : 0.0f;
       }
     }
     __syncthreads();
@@ -465,57 +497,126 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
       tc[s2] = acc;
     }
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) Tl[(b8 + s2) * LD + b8 + c8] = tc[s2];
+    for (int s2 = 0; s2 < 8; ++s2) Tl[(b8 + s2) * TP + b8 + c8] = tc[s2];
   }
   __syncthreads();
   const int pq = tid >> 6, i8 = (tid >> 3) & 7, j8 = tid & 7, o8 = 16 * pq;
   if (tid < 128) {  // W = M_10 T_00 of the pair of blocks starting at row o8
     float w = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w = __builtin_fmaf(Ml[(o8 + 8 + i8) * LD + o8 + k], Tl[(o8 + k) * LD + o8 + j8], w);
+    for (int k = 0; k < 8; ++k) w = __builtin_fmaf(Ml[(o8 + 8 + i8) * LD + o8 + k], Tl[(o8 + k) * TP + o8 + j8], w);
     Wl[pq * 64 + i8 * 8 + j8] = w;
   }
   __syncthreads();
   if (tid < 128) {  // T_10 = -T_11 W
     float t = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t = __builtin_fmaf(Tl[(o8 + 8 + i8) * LD + o8 + 8 + k], Wl[pq * 64 + k * 8 + j8], t);
-    Tl[(o8 + 8 + i8) * LD + o8 + j8] = -t;
+    for (int k = 0; k < 8; ++k) t = __builtin_fmaf(Tl[(o8 + 8 + i8) * TP + o8 + 8 + k], Wl[pq * 64 + k * 8 + j8], t);
+    Tl[(o8 + 8 + i8) * TP + o8 + j8] = -t;
   }
   __syncthreads();
   const int i16 = tid >> 4, j16 = tid & 15;
   {  // the same on the two halves of 16 rows
     float w = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) w = __builtin_fmaf(Ml[(16 + i16) * LD + k], Tl[k * LD + j16], w);
+    for (int k = 0; k < 16; ++k) w = __builtin_fmaf(Ml[(16 + i16) * LD + k], Tl[k * TP + j16], w);
     Wl[i16 * 16 + j16] = w;
   }
   __syncthreads();
   {
     float t = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) t = __builtin_fmaf(Tl[(16 + i16) * LD + 16 + k], Wl[k * 16 + j16], t);
-    Tl[(16 + i16) * LD + j16] = -t;
+    for (int k = 0; k < 16; ++k) t = __builtin_fmaf(Tl[(16 + i16) * TP + 16 + k], Wl[k * 16 + j16], t);
+    Tl[(16 + i16) * TP + j16] = -t;
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += 256) rec[kRecT + e] = Tl[(e / C) * LD + e % C];
-  // keys, queries and the decays
-  for (int q4 = tid; q4 < C * DK / 4; q4 += 256) {
-    const int s2 = q4 / (DK / 4), k4 = q4 % (DK / 4);
-    reinterpret_cast<float4*>(rec + kRecK)[q4] = *reinterpret_cast<const float4*>(kl + s2 * KP + 4 * k4);
-    reinterpret_cast<float4*>(rec + RQ)[q4] = *reinterpret_cast<const float4*>(ql + s2 * KP + 4 * k4);
+  // U = T diag(beta gamma) Kh, then Q' = diag(gamma) Qh - P U, 32 columns per wave at a time on
+  // v_mfma_f32_32x32x2_f32. Step j of 16 takes k = 16 (l / 32) + j: lane l supplies T[l % 32][k]
+  // (or P) and the k-th row's entry in column l % 32; result register i of lane l is row
+  // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
+  const int m = lane & 31, hs = lane >> 5;
+  f32x4_t ta[4], pa[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ta[q] = *reinterpret_cast<const f32x4_t*>(Tl + m * TP + 16 * hs + 4 * q);
+    pa[q] = *reinterpret_cast<const f32x4_t*>(Pl + m * TP + 16 * hs + 4 * q);
   }
-  if (tid < C) {
-    const float Gl = Gs[n - 1];
-    rec[RS + tid] = __expf(Gs[tid]);
-    rec[RS + C + tid] = tid < n ? __expf(Gl - Gs[tid]) : 0.0f;
-    rec[RS + 2 * C + tid] = bl[tid];
-    if (tid == 0) rec[RS + 3 * C] = __expf(Gl);
+  float* sw = Sw[wave];
+  for (int ct = wave; ct < DK / 32; ct += 4) {
+    const int c0 = 32 * ct;
+    f32x16_t u = {};
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int k = 16 * hs + jj;
+      u = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[jj >> 2][jj & 3], bgl[k] * kl[k * KP + c0 + m], u, 0, 0, 0);
+    }
+    f32x16_t y;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
+      rec[(size_t)s2 * DK + c0 + m] = u[i];
+      sw[s2 * LD + m] = u[i];
+      y[i] = gam[s2] * ql[s2 * KP + c0 + m];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int k = 16 * hs + jj;
+      y = __builtin_amdgcn_mfma_f32_32x32x2f32(-pa[jj >> 2][jj & 3], sw[k * LD + m], y, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rec[oQ + (size_t)(8 * (i >> 2) + 4 * hs + (i & 3)) * DK + c0 + m] = y[i];
+    wave_lds_sync();  // sw is rewritten by the next column block
   }
+  // Vb = T diag(beta) V and O' = P Vb, 32 state rows per wave at a time (rows past dv are zero
+  // and not stored)
+  for (int vt = wave; vt < (dv + 31) / 32; vt += 4) {
+    const int r = 32 * vt + m;
+    const bool rok = r < dv;
+    if (vt != wave) load_v(vt);
+    f32x16_t u = {};
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int k = 16 * hs + jj;  // beta is zero past the last token
+      u = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[jj >> 2][jj & 3], rok ? bl[k] * bf16_to_f32(vr[jj]) : 0.0f,
+                                              u, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
+      if (rok) rec[oVB + (size_t)s2 * dv + r] = u[i];
+      sw[s2 * LD + m] = u[i];
+    }
+    wave_lds_sync();
+    f32x16_t y = {};
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int k = 16 * hs + jj;
+      y = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[jj >> 2][jj & 3], sw[k * LD + m], y, 0, 0, 0);
+    }
+    if (rok) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rec[oOB + (size_t)(8 * (i >> 2) + 4 * hs + (i & 3)) * dv + r] = y[i];
+    }
+    wave_lds_sync();
+  }
+  // kh transposed, and the decays
+  for (int e = tid; e < C * DK; e += 256) rec[oKT + e] = kl[(e % C) * KP + e / C];
+  if (tid < C) rec[oSC + tid] = tid < n ? __expf(Gs[n - 1] - Gs[tid]) : 0.0f;
+  if (tid == 0) rec[oSC + C] = __expf(Gs[n - 1]);
 }
 
 template <int DK>
 constexpr int delta_chunk_waves() { return DK / 16 < 8 ? DK / 16 : 8; }
+
+// One chunk's record entries held by a lane of k_delta_chunk
+template <int NTL, int NPR>
+struct DeltaChunkRegs {
+  f32x4_t ua[NTL][2], qa[NTL][2];  // U and Q': rows 16 h + l % 16, columns c0 + 4 (l / 16) .. + 3
+  f32x4_t kt[NTL][2];              // kh^T: column c0 + l % 16, tokens 8 (l / 16) .. + 7
+  float vb[NPR], ob[NPR], dc[NPR];  // Vb, O' and the decay of this thread's (token, row) pairs
+  float gl;                         // exp(G_last)
+};
 
 template <int DK>
 __global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(DeltaArgs a, const float* __restrict__ ws,
@@ -524,28 +625,19 @@ __global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(De
   constexpr int NW = delta_chunk_waves<DK>();   // wave w owns state columns [w*DK/NW, (w+1)*DK/NW)
   constexpr int NTH = 64 * NW;
   constexpr int NTL = DK / 16 / NW;             // 16-column state tiles per wave
-  constexpr int KP = DK + 4;                    // padded LDS row of kh / qh
-  constexpr int CP = C + 4;                     // padded LDS row of T / P and of the [row][token] buffers
-  constexpr int RF = delta_rec_floats<DK>();
-  constexpr int RQ = kRecK + C * DK, RS = kRecK + 2 * C * DK;
-  constexpr int NF4 = RF / 4;                   // float4 pieces of a record
-  constexpr int PER = (NF4 + NTH - 1) / NTH;    // pieces per thread
+  constexpr int CP = C + 4;                     // LDS row of W ([row][token])
   constexpr int NPR = RW * C / NTH;             // (token, row) pairs per thread
   static_assert(RW == 16 && NTL >= 1 && NPR >= 1 && RW * C % NTH == 0, "16 rows, whole tiles");
-  __shared__ __attribute__((aligned(16))) float kl[C * KP];
-  __shared__ __attribute__((aligned(16))) float ql[C * KP];
-  __shared__ __attribute__((aligned(16))) float Tl[C * CP];
-  __shared__ __attribute__((aligned(16))) float Pl[C * CP];
-  __shared__ __attribute__((aligned(16))) float scl[128];
-  __shared__ float part[NW][2][C * RW];  // each wave's share of X and Y, [token][row]
-  __shared__ float vl[C * RW];           // v, [token][row]
-  __shared__ __attribute__((aligned(16))) float Rt[RW * CP];  // R, [row][token]
-  __shared__ __attribute__((aligned(16))) float Dt[RW * CP];  // delta, [row][token]
-  __shared__ float Wt[RW * CP];          // exp(G_last - G_s) delta, [row][token]
+  __shared__ float part[NW][2][C * RW];  // each wave's share of U S0^T and Q' S0^T, [token][row]
+  __shared__ __attribute__((aligned(16))) float Wt[RW * CP];  // exp(G_last - G_s) delta, [row][token]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = blockIdx.x, b = blockIdx.z, r0 = blockIdx.y * RW;
   const int m16 = lane & 15, q4 = lane >> 4;
+  const int dv = a.dv;
+  const size_t RF = delta_rec_floats(DK, dv);
+  const size_t oQ = (size_t)C * DK, oKT = 2 * oQ, oVB = 3 * oQ, oOB = oVB + (size_t)C * dv,
+               oSC = oOB + (size_t)C * dv;
 
   // The state in the accumulator layout of v_mfma_f32_16x16x4_f32, as S^T tiles [column][row]:
   // register i of lane l in tile u holds S[r0 + l % 16][c0 + 4 (l / 16) + i], c0 = 16 (w NTL + u).
@@ -553,67 +645,45 @@ __global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(De
 #pragma unroll
   for (int u = 0; u < NTL; ++u) {
     const int c0 = 16 * (wave * NTL + u);
-    const size_t src = (((size_t)b * a.Hv + j) * a.dv + r0 + m16) * DK + c0 + 4 * q4;
+    const size_t src = (((size_t)b * a.Hv + j) * dv + r0 + m16) * DK + c0 + 4 * q4;
     st[u] = a.s_in ? *reinterpret_cast<const f32x4_t*>(a.s_in + src) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // a chunk's record and v values in registers, then into LDS
-  f32x4_t pr[PER];  // a native vector type: an array of it stays in registers
-  uint16_t pvb[NPR];  // v as raw bits: converted in stash, so fetch never waits
-  bool pvok[NPR];
-  auto fetch = [&](int cc) __attribute__((always_inline)) {
-    const f32x4_t* rec = reinterpret_cast<const f32x4_t*>(ws + (((size_t)b * a.Hv + j) * nchunks + cc) * RF);
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int q = tid + NTH * u;
-      pr[u] = rec[q < NF4 ? q : NF4 - 1];
-    }
-#pragma unroll
-    for (int e = 0; e < NPR; ++e) {
-      const int p = tid + NTH * e, t = cc * C + p / RW;
-      pvok[e] = t < a.T;
-      pvb[e] = a.v[(((size_t)b * a.T + (pvok[e] ? t : a.T - 1)) * a.Hv + j) * a.dv + r0 + p % RW];
-    }
-  };
-  auto stash = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int q = tid + NTH * u, f = 4 * q;
-      if (q >= NF4) continue;  // only the last piece index can be past the record
-      float* dst;
-      if (f < kRecP) dst = Tl + (f / C) * CP + f % C;
-      else if (f < kRecK) dst = Pl + ((f - kRecP) / C) * CP + (f - kRecP) % C;
-      else if (f < RQ) dst = kl + ((f - kRecK) / DK) * KP + (f - kRecK) % DK;
-      else if (f < RS) dst = ql + ((f - RQ) / DK) * KP + (f - RQ) % DK;
-      else dst = scl + (f - RS);
-      *reinterpret_cast<f32x4_t*>(dst) = pr[u];
-    }
-#pragma unroll
-    for (int e = 0; e < NPR; ++e) vl[tid + NTH * e] = pvok[e] ? bf16_to_f32(pvb[e]) : 0.0f;
-  };
-
-  fetch(0);
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const int t0 = cc * C;
-    __syncthreads();  // the previous chunk is done with every LDS buffer
-    stash();
-    if (cc + 1 < nchunks) fetch(cc + 1);  // in flight while this chunk is computed
-    __syncthreads();
-    // X[s][r] = kh_s . S0_r and Y[s][r] = qh_s . S0_r over this wave's columns, two 16-token
-    // tiles each: A = kh or qh [token][column], B = the state tile; lanes l / 16 = 0..3 supply
-    // columns c0 + 4 (l / 16) + i in step i, the same columns their state registers hold
-    f32x4_t ax[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    f32x4_t ay[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  using Regs = DeltaChunkRegs<NTL, NPR>;
+  auto fetch = [&](int cc, Regs& R) __attribute__((always_inline)) {
+    const float* rec = ws + (((size_t)b * a.Hv + j) * nchunks + cc) * RF;
 #pragma unroll
     for (int u = 0; u < NTL; ++u) {
       const int c0 = 16 * (wave * NTL + u);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kl + (16 * h + m16) * KP + c0 + 4 * q4);
-        const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(ql + (16 * h + m16) * KP + c0 + 4 * q4);
+        R.ua[u][h] = *reinterpret_cast<const f32x4_t*>(rec + (size_t)(16 * h + m16) * DK + c0 + 4 * q4);
+        R.qa[u][h] = *reinterpret_cast<const f32x4_t*>(rec + oQ + (size_t)(16 * h + m16) * DK + c0 + 4 * q4);
+        R.kt[u][h] = *reinterpret_cast<const f32x4_t*>(rec + oKT + (size_t)(c0 + m16) * C + 8 * q4 + 4 * h);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NPR; ++e) {
+      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
+      R.vb[e] = rec[oVB + (size_t)s2 * dv + r0 + r];
+      R.ob[e] = rec[oOB + (size_t)s2 * dv + r0 + r];
+      R.dc[e] = rec[oSC + s2];
+    }
+    R.gl = rec[oSC + C];
+  };
+  auto body = [&](int cc, const Regs& R) __attribute__((always_inline)) {
+    const int t0 = cc * C;
+    // U S0^T and Q' S0^T over this wave's columns, two 16-token tiles each: lanes l / 16 = 0..3
+    // supply columns c0 + 4 (l / 16) + i in step i, the same columns their state registers hold
+    f32x4_t ad[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4_t ao[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int u = 0; u < NTL; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ax[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], st[u][i], ax[h], 0, 0, 0);
-          ay[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[i], st[u][i], ay[h], 0, 0, 0);
+          ad[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(R.ua[u][h][i], st[u][i], ad[h], 0, 0, 0);
+          ao[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(R.qa[u][h][i], st[u][i], ao[h], 0, 0, 0);
         }
       }
     }
@@ -622,13 +692,12 @@ __global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(De
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        part[wave][0][(16 * h + 4 * q4 + i) * RW + m16] = ax[h][i];
-        part[wave][1][(16 * h + 4 * q4 + i) * RW + m16] = ay[h][i];
+        part[wave][0][(16 * h + 4 * q4 + i) * RW + m16] = ad[h][i];
+        part[wave][1][(16 * h + 4 * q4 + i) * RW + m16] = ao[h][i];
       }
     }
     __syncthreads();
-    // the waves' shares added; R = beta (v - exp(G) X) stored [row][token]; exp(G) Y kept
-    float gy[NPR];
+    // delta = Vb - U S0^T and o = O' + Q' S0^T, the waves' shares added in wave order
 #pragma unroll
     for (int e = 0; e < NPR; ++e) {
       const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
@@ -638,59 +707,39 @@ __global__ __launch_bounds__(64 * delta_chunk_waves<DK>()) void k_delta_chunk(De
         x += part[w][0][p];
         y += part[w][1][p];
       }
-      gy[e] = scl[s2] * y;
-      Rt[r * CP + s2] = scl[2 * C + s2] * (vl[p] - scl[s2] * x);
+      if (t0 + s2 < a.T) a.o[(((size_t)b * a.T + t0 + s2) * a.Hv + j) * dv + r0 + r] = R.ob[e] + y;
+      Wt[r * CP + s2] = R.dc[e] * (R.vb[e] - x);
     }
     __syncthreads();
-    // delta_s = sum_r T[s][r] R_r (T is zero above its diagonal), and the update weights
-#pragma unroll
-    for (int e = 0; e < NPR; ++e) {
-      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
-      float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-      for (int k4 = 0; k4 < C / 4; k4 += 2) {
-        d0 += dot4(*reinterpret_cast<const float4*>(Tl + s2 * CP + 4 * k4),
-                   *reinterpret_cast<const float4*>(Rt + r * CP + 4 * k4));
-        d1 += dot4(*reinterpret_cast<const float4*>(Tl + s2 * CP + 4 * k4 + 4),
-                   *reinterpret_cast<const float4*>(Rt + r * CP + 4 * k4 + 4));
-      }
-      Dt[r * CP + s2] = d0 + d1;
-      Wt[r * CP + s2] = scl[C + s2] * (d0 + d1);
-    }
-    __syncthreads();
-    // o_s = exp(G_s) qh_s . S0 + sum_r P[s][r] delta_r
-#pragma unroll
-    for (int e = 0; e < NPR; ++e) {
-      const int p = tid + NTH * e, s2 = p / RW, r = p % RW;
-      float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-      for (int k4 = 0; k4 < C / 4; k4 += 2) {
-        o0 += dot4(*reinterpret_cast<const float4*>(Pl + s2 * CP + 4 * k4),
-                   *reinterpret_cast<const float4*>(Dt + r * CP + 4 * k4));
-        o1 += dot4(*reinterpret_cast<const float4*>(Pl + s2 * CP + 4 * k4 + 4),
-                   *reinterpret_cast<const float4*>(Dt + r * CP + 4 * k4 + 4));
-      }
-      if (t0 + s2 < a.T)
-        a.o[(((size_t)b * a.T + t0 + s2) * a.Hv + j) * a.dv + r0 + r] = gy[e] + (o0 + o1);
-    }
-    // S^T = exp(G_last) S0^T + kh^T W on the state tiles: A = kh [column][token], B = W
-    // [token][row]; lanes l / 16 = 0..3 supply token 4 k + l / 16 in step k
-    const float gl = scl[3 * C];
+    // S^T = exp(G_last) S0^T + kh^T W on the state tiles: A = kh^T [column][token], B = W
+    // [token][row]; lanes l / 16 = 0..3 supply tokens 8 (l / 16) + k in step k
 #pragma unroll
     for (int u = 0; u < NTL; ++u) {
-      const int c0 = 16 * (wave * NTL + u);
-      st[u] *= gl;
+      st[u] *= R.gl;
 #pragma unroll
-      for (int k = 0; k < C / 4; ++k) {
-        const int s2 = 4 * k + q4;
-        st[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(kl[s2 * KP + c0 + m16], Wt[m16 * CP + s2], st[u], 0, 0, 0);
-      }
+      for (int k = 0; k < 8; ++k)
+        st[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(R.kt[u][k >> 2][k & 3], Wt[m16 * CP + 8 * q4 + k],
+                                                     st[u], 0, 0, 0);
     }
+  };
+  // two register sets, so that a chunk's entries are requested while the previous one runs;
+  // the requests are unconditional (past the end they repeat the last chunk's), so that the
+  // wait before each chunk counts only the other set's requests (three sets, two chunks
+  // ahead, were no faster)
+  Regs ra, rb;
+  fetch(0, ra);
+  for (int cc = 0;; cc += 2) {
+    fetch(min(cc + 1, nchunks - 1), rb);
+    body(cc, ra);
+    if (cc + 1 >= nchunks) break;
+    fetch(min(cc + 2, nchunks - 1), ra);
+    body(cc + 1, rb);
+    if (cc + 2 >= nchunks) break;
   }
 #pragma unroll
   for (int u = 0; u < NTL; ++u) {
     const int c0 = 16 * (wave * NTL + u);
-    const size_t dst = (((size_t)b * a.Hv + j) * a.dv + r0 + m16) * DK + c0 + 4 * q4;
+    const size_t dst = (((size_t)b * a.Hv + j) * dv + r0 + m16) * DK + c0 + 4 * q4;
     *reinterpret_cast<f32x4_t*>(a.s_out + dst) = st[u];
   }
 }
@@ -730,12 +779,6 @@ int delta_prologue(const delta_rule_desc_t* desc, const uint16_t* q, const uint1
   return MOE_OK;
 }
 
-size_t delta_rec_bytes(int dk) {
-  const int rf = dk == 64 ? delta_rec_floats<64>() : dk == 128 ? delta_rec_floats<128>()
-                                                               : delta_rec_floats<256>();
-  return (size_t)rf * sizeof(float);
-}
-
 }  // namespace
 
 extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t* q,
@@ -765,11 +808,11 @@ extern "C" int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t*
 
 extern "C" size_t delta_rule_chunked_workspace_bytes(const delta_rule_desc_t* desc,
                                                      int32_t batch, int32_t T) {
-  if (!desc || batch <= 0 || T <= 0 || desc->num_v_heads <= 0) return 0;
+  if (!desc || batch <= 0 || T <= 0 || desc->num_v_heads <= 0 || desc->dv <= 0) return 0;
   const int dk = desc->dk;
   if (dk != 64 && dk != 128 && dk != 256) return 0;
   const size_t nch = ((size_t)T + kDeltaChunk - 1) / kDeltaChunk;
-  return (size_t)batch * desc->num_v_heads * nch * delta_rec_bytes(dk);
+  return (size_t)batch * desc->num_v_heads * nch * delta_rec_floats(dk, desc->dv) * sizeof(float);
 }
 
 extern "C" int delta_rule_forward_chunked(const delta_rule_desc_t* desc, const uint16_t* q,

@@ -58,8 +58,9 @@ int delta_rule_forward(const delta_rule_desc_t* desc, const uint16_t* q, const u
  * chunks at once and the state advances one chunk per step. For long T (prefill).
  *   workspace  device buffer of at least delta_rule_chunked_workspace_bytes(desc, batch, T)
  *              bytes, 16-byte aligned; its contents on entry do not matter and are overwritten
- *              (per (sequence, value head, chunk): the chunk's matrices, normalised keys and
- *              queries and decays). Calls that share a workspace must not overlap.
+ *              (per (sequence, value head, chunk): the chunk's corrected keys and queries,
+ *              its value terms, its normalised keys and its decays; 4 * (96 dk + 64 dv + 64)
+ *              bytes per record). Calls that share a workspace must not overlap.
  * Returns MOE_WORKSPACE_TOO_SMALL when ws_bytes is below the size needed, else as
  * delta_rule_forward. */
 size_t delta_rule_chunked_workspace_bytes(const delta_rule_desc_t* desc, int32_t batch, int32_t T);

@@ -87,10 +87,12 @@ def test_delta_rule_chunked_sizes_and_rejections():
     from bit_grouped_gemm_amd import delta_rule as DR
     L = DR._lib()
     ok = DR.desc(16, 16, 128, 128)
-    # 16 chunks of 32 tokens x 16 heads, each record T and P (2 x 32 x 32), kh and qh
-    # (2 x 32 x 128) and 128 scalars, fp32
-    assert DR.chunked_workspace_bytes(ok, 1, 512) == 16 * 16 * (2048 + 8192 + 128) * 4
-    assert DR.chunked_workspace_bytes(ok, 2, 33) == 2 * 16 * 2 * (2048 + 8192 + 128) * 4
+    # 16 chunks of 32 tokens x 16 heads, each record three 32 x dk matrices, two 32 x dv
+    # matrices and 64 scalars, fp32
+    rec = 3 * 32 * 128 + 2 * 32 * 128 + 64
+    assert DR.chunked_workspace_bytes(ok, 1, 512) == 16 * 16 * rec * 4
+    assert DR.chunked_workspace_bytes(ok, 2, 33) == 2 * 16 * 2 * rec * 4
+    assert DR.chunked_workspace_bytes(DR.desc(2, 4, 256, 48), 1, 40) == 4 * 2 * (3 * 32 * 256 + 2 * 32 * 48 + 64) * 4
     assert DR.chunked_workspace_bytes(ok, 1, 0) == 0
     assert DR.chunked_workspace_bytes(DR.desc(16, 16, 96, 128), 1, 64) == 0
     call = lambda d, B=1, T=64, ws=FAKE, n=1 << 30: L.delta_rule_forward_chunked(  # noqa: E731
