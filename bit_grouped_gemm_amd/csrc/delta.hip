@@ -355,9 +355,11 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
   __shared__ __attribute__((aligned(16))) float Tl[C * TP];  // (I + M)^-1, built block by block
   __shared__ __attribute__((aligned(16))) float Pl[C * TP];  // P (lower triangular)
   __shared__ float Xl[2][C * LD];        // the dot products' second halves
-  __shared__ float Sw[4][C * LD];        // per wave: a 32 x 32 result on its way to a B operand
+  __shared__ __attribute__((aligned(16))) float Sw[4][C * TP];  // per wave: a 32 x 32 result,
+                                                                // transposed, on its way to a B operand
   __shared__ float Wl[16 * 16];
-  __shared__ float Gs[C], bl[C], gam[C], bgl[C];
+  __shared__ float Gs[C], bl[C], gam[C];
+  __shared__ __attribute__((aligned(16))) float bgl[C];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
@@ -532,41 +534,57 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
   __syncthreads();
   // U = T diag(beta gamma) Kh, then Q' = diag(gamma) Qh - P U, 32 columns per wave at a time on
   // v_mfma_f32_32x32x2_f32. Step j of 16 takes k = 16 (l / 32) + j: lane l supplies T[l % 32][k]
-  // (or P) and the k-th row's entry in column l % 32; result register i of lane l is row
+  // (or P) and the k-th row's entry in column l % 32 (the intermediate products are kept
+  // transposed, so both operands are read as 16-byte pieces); result register i of lane l is row
   // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
   const int m = lane & 31, hs = lane >> 5;
-  f32x4_t ta[4], pa[4];
+  f32x4_t ta[4], pa[4], bg[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     ta[q] = *reinterpret_cast<const f32x4_t*>(Tl + m * TP + 16 * hs + 4 * q);
     pa[q] = *reinterpret_cast<const f32x4_t*>(Pl + m * TP + 16 * hs + 4 * q);
+    bg[q] = *reinterpret_cast<const f32x4_t*>(bgl + 16 * hs + 4 * q);
   }
   float* sw = Sw[wave];
+  // a 32 x 32 result into sw transposed: register 4g + x is row 8g + 4 (l / 32) + x, column l % 32
+  auto stash_t = [&](const f32x16_t& u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4_t*>(sw + m * TP + 8 * g4 + 4 * hs) =
+          f32x4_t{u[4 * g4], u[4 * g4 + 1], u[4 * g4 + 2], u[4 * g4 + 3]};
+  };
   for (int ct = wave; ct < DK / 32; ct += 4) {
     const int c0 = 32 * ct;
+    f32x4_t kt[4];  // kh[16 (l / 32) + 4q .. + 3][c0 + l % 32], which is also its record row
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) kt[q][x] = kl[(16 * hs + 4 * q + x) * KP + c0 + m];
+      *reinterpret_cast<f32x4_t*>(rec + oKT + (size_t)(c0 + m) * C + 16 * hs + 4 * q) = kt[q];
+    }
     f32x16_t u = {};
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int k = 16 * hs + jj;
-      u = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[jj >> 2][jj & 3], bgl[k] * kl[k * KP + c0 + m], u, 0, 0, 0);
-    }
+    for (int jj = 0; jj < 16; ++jj)
+      u = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[jj >> 2][jj & 3], bg[jj >> 2][jj & 3] * kt[jj >> 2][jj & 3],
+                                              u, 0, 0, 0);
+    stash_t(u);
     f32x16_t y;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
       rec[(size_t)s2 * DK + c0 + m] = u[i];
-      sw[s2 * LD + m] = u[i];
       y[i] = gam[s2] * ql[s2 * KP + c0 + m];
     }
     wave_lds_sync();
+    f32x4_t ub[4];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int k = 16 * hs + jj;
-      y = __builtin_amdgcn_mfma_f32_32x32x2f32(-pa[jj >> 2][jj & 3], sw[k * LD + m], y, 0, 0, 0);
-    }
+    for (int q = 0; q < 4; ++q) ub[q] = *reinterpret_cast<const f32x4_t*>(sw + m * TP + 16 * hs + 4 * q);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      y = __builtin_amdgcn_mfma_f32_32x32x2f32(-pa[jj >> 2][jj & 3], ub[jj >> 2][jj & 3], y, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) rec[oQ + (size_t)(8 * (i >> 2) + 4 * hs + (i & 3)) * DK + c0 + m] = y[i];
-    wave_lds_sync();  // sw is rewritten by the next column block
+    wave_lds_sync();  // sw is rewritten by the next block
   }
   // Vb = T diag(beta) V and O' = P Vb, 32 state rows per wave at a time (rows past dv are zero
   // and not stored)
@@ -581,27 +599,26 @@ __global__ __launch_bounds__(256) void k_delta_prep(DeltaArgs a, float* __restri
       u = __builtin_amdgcn_mfma_f32_32x32x2f32(ta[jj >> 2][jj & 3], rok ? bl[k] * bf16_to_f32(vr[jj]) : 0.0f,
                                               u, 0, 0, 0);
     }
+    stash_t(u);
+    if (rok) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s2 = 8 * (i >> 2) + 4 * hs + (i & 3);
-      if (rok) rec[oVB + (size_t)s2 * dv + r] = u[i];
-      sw[s2 * LD + m] = u[i];
+      for (int i = 0; i < 16; ++i) rec[oVB + (size_t)(8 * (i >> 2) + 4 * hs + (i & 3)) * dv + r] = u[i];
     }
     wave_lds_sync();
+    f32x4_t ub[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ub[q] = *reinterpret_cast<const f32x4_t*>(sw + m * TP + 16 * hs + 4 * q);
     f32x16_t y = {};
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int k = 16 * hs + jj;
-      y = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[jj >> 2][jj & 3], sw[k * LD + m], y, 0, 0, 0);
-    }
+    for (int jj = 0; jj < 16; ++jj)
+      y = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[jj >> 2][jj & 3], ub[jj >> 2][jj & 3], y, 0, 0, 0);
     if (rok) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) rec[oOB + (size_t)(8 * (i >> 2) + 4 * hs + (i & 3)) * dv + r] = y[i];
     }
     wave_lds_sync();
   }
-  // kh transposed, and the decays
-  for (int e = tid; e < C * DK; e += 256) rec[oKT + e] = kl[(e % C) * KP + e / C];
+  // the decays
   if (tid < C) rec[oSC + tid] = tid < n ? __expf(Gs[n - 1] - Gs[tid]) : 0.0f;
   if (tid == 0) rec[oSC + C] = __expf(Gs[n - 1]);
 }
