@@ -407,11 +407,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4_gate_up(GemmParams p, int ns
 #undef MOE_GEMM_BLOCK
 }
 
+// Work unit u of the small-batch kernels (units are dispatched in order of u, round-robin over
+// the XCDs) -> block-map entry j and piece hb: first every piece of the shared expert's tiles
+// (tall: T rows), then the first piece of every routed tile, then the second pieces, and so
+// on. The tall tiles' pieces then start in the first round, spread over all XCDs, instead of
+// trailing the grid on the XCDs of their tiles; units past the last piece return at once.
+__device__ __forceinline__ bool small_unit(int u, int nb, int nsh, int pieces, int& j, int& hb) {
+  const int ns = nsh * pieces;
+  if (u < ns) {
+    j = nb - nsh + u / pieces;
+    hb = u % pieces;
+    return true;
+  }
+  const int nr = nb - nsh, r = u - ns;
+  if (nr <= 0) return false;
+  hb = r / nr;
+  j = r % nr;
+  return hb < pieces;
+}
+
 // Gate/up for small batches (few rows per expert): block-map tiles are cut into pieces of at
 // most 64 rows (two row tiles), one per workgroup, and two workgroups share a CU, so that one
 // wave's dequantisation (most of the work when a chunk feeds only one or two row tiles) runs
-// while the other wave waits for memory or issues MFMAs. Work units are the first pieces of
-// all tiles (the shared expert's first), then the second, third and fourth pieces.
+// while the other wave waits for memory or issues MFMAs. Units are ordered by small_unit.
 constexpr int kGUSRows = 64;
 __global__ __launch_bounds__(256, 2) void k_gemm_w4_gate_up_small(GemmParams p, int nslices) {
   constexpr int MODE = kGateUp;
@@ -423,16 +441,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4_gate_up_small(GemmParams p, 
 
   const int nb = *p.num_blocks;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int hd = kXcds * (local / nslices) + xcd;  // work unit
   const int slice = local % nslices;
   constexpr int kPieces = kBlockM / kGUSRows;
-  const int rounds = (gridDim.x / kXcds) / nslices;  // units per quarter of the grid / kXcds
-  const int piece_units = kXcds * (rounds / kPieces);
-  const int hb = hd / piece_units;
-  const int jd = hd - hb * piece_units;
-  if (jd >= nb) return;
   const int nsh = p.n_shared > 0 ? (p.TK / p.K + kBlockM - 1) / kBlockM : 0;
-  const int j = jd < nsh ? nb - nsh + jd : jd - nsh;  // block-map entry
+  int j, hb;  // the unit's block-map entry and piece (all slices of a unit on one XCD)
+  if (!small_unit(kXcds * (local / nslices) + xcd, nb, nsh, kPieces, j, hb)) return;
   const int4 blk = p.blocks[j];
   const int e = blk.x;
   const int m_len = blk.z - kGUSRows * hb;
@@ -709,8 +722,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4_down(GemmParams p, int nslic
 
 // Down projection for small batches (the same condition as k_gemm_w4_gate_up_small): pieces of
 // at most 32 rows (one row tile) with 8 KiB chunk buffers, so that four workgroups share a CU
-// and one workgroup's dequantisation overlaps the others' loads. Work units are the first
-// pieces of all tiles, then the second, and so on; units without rows return at once.
+// and one workgroup's dequantisation overlaps the others' loads. Units are ordered by
+// small_unit; units without rows return at once.
 template <int MODE>
 __global__ __launch_bounds__(256, 4) void k_gemm_w4_down_small(GemmParams p, int nslices) {
   constexpr int kRowsS = 32;
@@ -719,13 +732,10 @@ __global__ __launch_bounds__(256, 4) void k_gemm_w4_down_small(GemmParams p, int
   __shared__ __attribute__((aligned(1024))) char lds1[kRowsS * kDRowBytes];
   const int nb = *p.num_blocks;
   const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
-  const int hd = kXcds * (local / nslices) + xcd;  // work unit
   const int slice = local % nslices;
-  const int rounds = (gridDim.x / kXcds) / nslices;
-  const int piece_units = kXcds * (rounds / kPieces);
-  const int hb = hd / piece_units;
-  const int j = hd - hb * piece_units;
-  if (j >= nb) return;
+  const int nsh = p.n_shared > 0 ? (p.TK / p.K + kBlockM - 1) / kBlockM : 0;
+  int j, hb;  // the unit's block-map entry and piece (all slices of a unit on one XCD)
+  if (!small_unit(kXcds * (local / nslices) + xcd, nb, nsh, kPieces, j, hb)) return;
   const int4 blk = p.blocks[j];
   const int e = blk.x;
   const int m_len = blk.z - kRowsS * hb;
