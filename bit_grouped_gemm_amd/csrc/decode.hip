@@ -132,27 +132,34 @@ __device__ __forceinline__ void pair_dots(const PairW& w, const uint16_t* xs, in
   dequant8(w.u.y, us, ub, du + 4);
   dequant8(w.u.z, us, ub, du + 8);
   dequant8(w.u.w, us, ub, du + 12);
+  auto token_dots = [&](int j, int t) __attribute__((always_inline)) {
+    const uint4* xr = reinterpret_cast<const uint4*>(xs + (size_t)t * H + 32 * lane);
+    float ag = 0.0f, au = 0.0f;
 #pragma unroll
-  for (int j = 0; j < TC; ++j) {
-    if (j < m) {
-      const int t = tok ? tok[j] : j;
-      const uint4* xr = reinterpret_cast<const uint4*>(xs + (size_t)t * H + 32 * lane);
-      float ag = 0.0f, au = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 xv = xr[q];
-        ag = dot2_bf16(xv.x, dg[4 * q + 0], ag);
-        ag = dot2_bf16(xv.y, dg[4 * q + 1], ag);
-        ag = dot2_bf16(xv.z, dg[4 * q + 2], ag);
-        ag = dot2_bf16(xv.w, dg[4 * q + 3], ag);
-        au = dot2_bf16(xv.x, du[4 * q + 0], au);
-        au = dot2_bf16(xv.y, du[4 * q + 1], au);
-        au = dot2_bf16(xv.z, du[4 * q + 2], au);
-        au = dot2_bf16(xv.w, du[4 * q + 3], au);
-      }
-      v[2 * j] = ag;
-      v[2 * j + 1] = au;
+    for (int q = 0; q < 4; ++q) {
+      const uint4 xv = xr[q];
+      ag = dot2_bf16(xv.x, dg[4 * q + 0], ag);
+      ag = dot2_bf16(xv.y, dg[4 * q + 1], ag);
+      ag = dot2_bf16(xv.z, dg[4 * q + 2], ag);
+      ag = dot2_bf16(xv.w, dg[4 * q + 3], ag);
+      au = dot2_bf16(xv.x, du[4 * q + 0], au);
+      au = dot2_bf16(xv.y, du[4 * q + 1], au);
+      au = dot2_bf16(xv.z, du[4 * q + 2], au);
+      au = dot2_bf16(xv.w, du[4 * q + 3], au);
     }
+    v[2 * j] = ag;
+    v[2 * j + 1] = au;
+  };
+  if (!tok) {
+    // tokens 0..m-1 of the staged batch (m is the batch, usually TC): every entry is formed
+    // without a branch, entries past m from token 0 (never stored), so that the LDS reads of
+    // all tokens are issued together instead of one branch and one wait per token
+#pragma unroll
+    for (int j = 0; j < TC; ++j) token_dots(j, j < m ? j : 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < TC; ++j)
+      if (j < m) token_dots(j, tok[j]);
   }
 }
 
@@ -371,22 +378,22 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
           w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
+      // no branch per input piece or token: pieces past the row have zero weights and read
+      // the row's last piece of x, tokens past T read token 0 (their sums are never stored),
+      // so the LDS reads of all tokens are issued together
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int j = j0 + lane + 64 * i;
-        if (j < n4) {
+        const int j = min(j0 + lane + 64 * i, n4 - 1);
 #pragma unroll
-          for (int t = 0; t < TC; ++t) {
-            if (t < T) {
-              const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)t * H + 4 * j);
-              float a = acc[t];
-              a = __builtin_fmaf(bf16_to_f32(xv.x & 0xFFFFu), w[i].x, a);
-              a = __builtin_fmaf(bf16_to_f32(xv.x >> 16), w[i].y, a);
-              a = __builtin_fmaf(bf16_to_f32(xv.y & 0xFFFFu), w[i].z, a);
-              a = __builtin_fmaf(bf16_to_f32(xv.y >> 16), w[i].w, a);
-              acc[t] = a;
-            }
-          }
+        for (int t = 0; t < TC; ++t) {
+          const int tt = t < T ? t : 0;
+          const uint2 xv = *reinterpret_cast<const uint2*>(xs + (size_t)tt * H + 4 * j);
+          float a = acc[t];
+          a = __builtin_fmaf(bf16_to_f32(xv.x & 0xFFFFu), w[i].x, a);
+          a = __builtin_fmaf(bf16_to_f32(xv.x >> 16), w[i].y, a);
+          a = __builtin_fmaf(bf16_to_f32(xv.y & 0xFFFFu), w[i].z, a);
+          a = __builtin_fmaf(bf16_to_f32(xv.y >> 16), w[i].w, a);
+          acc[t] = a;
         }
       }
     }
