@@ -345,24 +345,57 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
   const int n4 = H >> 2;
   const int f = task - E - 1;
   const bool shared_task = !router && task < nA;
-  // the task's weights are requested before x is staged
   float4 w[8];
   PairW pw;
-  if (router) {
+  auto load_w = [&]() __attribute__((always_inline)) {
+    if (router) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = lane + 64 * i;
-      w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int i = 0; i < 8; ++i) {
+        const int j = lane + 64 * i;
+        w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else if (shared_task) {
+      load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
     }
-  } else if (shared_task) {
-    load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
-  }
+  };
   if (p.rin) {
-    // inside the stack: x from the residual stream (workgroup 0 also writes it for B)
+    // inside the stack: the task's weights first, then x from the residual stream (workgroup 0
+    // also writes it for B)
+    load_w();
     float* part = reinterpret_cast<float*>(xs + (size_t)T * H);
     norm_x(xs, p.rin, T, H, p.eps, blockIdx.x == 0 ? p.xw : nullptr, part);
   } else {
-    stage_x<TC, 256>(xs, p.x, (T * H) >> 3);
+    // x first (at most TC 16-byte pieces per thread, H <= 2048), then the task's weights: the
+    // staging then waits for x only, and the dot products take the weights as they arrive.
+    // The LDS writes sit inside each task branch so that the wait before them counts exactly
+    // that branch's weight requests.
+    const int n8 = (T * H) >> 3;
+    u32x4_t xt[TC];  // a native vector type: an array of it stays in registers
+#pragma unroll
+    for (int b = 0; b < TC; ++b) {
+      const int v = tid + 256 * b;
+      xt[b] = reinterpret_cast<const u32x4_t*>(p.x)[v < n8 ? v : n8 - 1];
+    }
+    auto store_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int b = 0; b < TC; ++b) {
+        const int v = tid + 256 * b;
+        if (v < n8) reinterpret_cast<u32x4_t*>(xs)[v] = xt[b];
+      }
+    };
+    if (router) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = lane + 64 * i;
+        w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      store_x();
+    } else if (shared_task) {
+      load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
+      store_x();
+    } else {
+      store_x();
+    }
     __syncthreads();
   }
 
