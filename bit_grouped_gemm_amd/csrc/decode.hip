@@ -732,24 +732,33 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
               acc = __builtin_fmaf(R.row_w[row0], one[0], acc);
             continue;
           }
+          // tokens in pairs: one branch per pair, both rows' activation reads issued
+          // together (the second row of a pair past m reads the first and is never taken)
           float dots[TC];
+          const bool lane_in = sl < (Kd >> 5);
+          const int sc = lane_in ? sl : 0;
 #pragma unroll
-          for (int j = 0; j < TC; ++j) {
-            dots[j] = 0.0f;
-            if (j < m && sl < (Kd >> 5)) {
-              const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)j * Fs
-                                      : abase + (size_t)(row0 + j) * F;
-              const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sl);
-              float s = 0.0f;
+          for (int j = 0; j < TC; ++j) dots[j] = 0.0f;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const uint4 a4 = av[q];
-                s = dot2_bf16(a4.x, wd[4 * q + 0], s);
-                s = dot2_bf16(a4.y, wd[4 * q + 1], s);
-                s = dot2_bf16(a4.z, wd[4 * q + 2], s);
-                s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+          for (int j = 0; j < TC; j += 2) {
+            if (j < m && lane_in) {
+#pragma unroll
+              for (int h = 0; h < 2 && j + h < TC; ++h) {
+                const int jr = j + h < m ? j + h : j;
+                const uint16_t* ar = sh ? abase + (size_t)TK * F + (size_t)jr * Fs
+                                        : abase + (size_t)(row0 + jr) * F;
+                const uint4* av = reinterpret_cast<const uint4*>(ar + 32 * sc);
+                float s = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const uint4 a4 = av[q];
+                  s = dot2_bf16(a4.x, wd[4 * q + 0], s);
+                  s = dot2_bf16(a4.y, wd[4 * q + 1], s);
+                  s = dot2_bf16(a4.z, wd[4 * q + 2], s);
+                  s = dot2_bf16(a4.w, wd[4 * q + 3], s);
+                }
+                dots[j + h] = s;
               }
-              dots[j] = s;
             }
           }
           group_reduce<TC, 16>(dots, sl);
