@@ -90,6 +90,12 @@ __device__ __forceinline__ void group_reduce(float (&v)[N], int r) {
 
 // One lane's share of a gate row and an up row: the 32-input chunk c = lane (H <= 2048: one
 // 16-byte load per row and lane, a 1 KiB row per wave).
+// A 16-byte weight word that is read once per call, as a non-temporal load.
+__device__ __forceinline__ uint4 load_once(const uint32_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct PairW {
   uint4 g, u;
   // raw bf16 bits, kept 16-bit so that the loaded value is the register itself (a widening at
@@ -104,8 +110,8 @@ __device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe
                                           size_t row, int H, int lane) {
   const int c = lane < (H >> 5) ? lane : (H >> 5) - 1;
   const size_t sidx = row * (size_t)(H >> 6) + (c >> 1);
-  w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[c];
-  w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[c];
+  w.g = load_once(G.q + row * (size_t)(H >> 3) + 4 * c);
+  w.u = load_once(U.q + row * (size_t)(H >> 3) + 4 * c);
   w.gs = G.scale[sidx];
   w.gb = G.bias[sidx];
   w.us = U.scale[sidx];
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
         const int h = h0 + 4 * r;
         const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
         const size_t g = row * (size_t)(Kd >> 6) + (c >> 1);
-        bt.w[b][r].q = reinterpret_cast<const uint4*>(q + row * (size_t)(Kd >> 3))[c];
+        bt.w[b][r].q = load_once(q + row * (size_t)(Kd >> 3) + 4 * c);
         bt.w[b][r].s = sp[g];
         bt.w[b][r].b = bp[g];
       }
