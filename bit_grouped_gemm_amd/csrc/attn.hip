@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
   };
   uint4 kv[U], vv[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) kv[u] = *krow(t0, u);
+  for (int u = 0; u < U; ++u) kv[u] = load_nt(krow(t0, u));
 #pragma unroll
-  for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(t0, u));
+  for (int u = 0; u < U; ++u) vv[u] = load_nt(row(a.vc, tok(t0, u)));
   uint4 qv[kMM ? NJ : HPW];
   if constexpr (kMM) {
     const int hq = lane & 15;  // B operand: head hq, dimensions 32j + 8*(lane / 16) .. + 8
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     }
     if (more) {   // the keys are used: request the next chunk's
 #pragma unroll
-      for (int u = 0; u < U; ++u) kv[u] = *krow(c0 + C, u);
+      for (int u = 0; u < U; ++u) kv[u] = load_nt(krow(c0 + C, u));
     }
     if constexpr (kMM) {  // the value rows to LDS, then the next chunk's requested
 #pragma unroll
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
       }
       if (more) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(c0 + C, u));
+        for (int u = 0; u < U; ++u) vv[u] = load_nt(row(a.vc, tok(c0 + C, u)));
       }
     }
     __syncthreads();
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_split(AttnArgs a) {
     }
     if (more) {   // the values are used: request the next chunk's
 #pragma unroll
-      for (int u = 0; u < U; ++u) vv[u] = *row(a.vc, tok(c0 + C, u));
+      for (int u = 0; u < U; ++u) vv[u] = load_nt(row(a.vc, tok(c0 + C, u)));
     }
     __syncthreads();   // the next chunk's scores overwrite sc and st
   }

@@ -90,12 +90,6 @@ __device__ __forceinline__ void group_reduce(float (&v)[N], int r) {
 
 // One lane's share of a gate row and an up row: the 32-input chunk c = lane (H <= 2048: one
 // 16-byte load per row and lane, a 1 KiB row per wave).
-// A 16-byte weight word that is read once per call, as a non-temporal load.
-__device__ __forceinline__ uint4 load_once(const uint32_t* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 struct PairW {
   uint4 g, u;
   // raw bf16 bits, kept 16-bit so that the loaded value is the register itself (a widening at
@@ -106,16 +100,29 @@ struct PairW {
 // Every load is unconditional (lanes past the row re-read its last chunk, whose products are
 // never used): a load whose destination is merged with a value from another branch has to be
 // copied, and the copy makes the wave wait for the load right away.
+// NT: non-temporal loads, for the routed experts' rows, which a decode step reads once and
+// which would otherwise displace from the caches the weights that every step reads again (the
+// router rows and the shared expert, about 3.5 MB per layer, loaded with ordinary loads).
+template <bool NT>
 __device__ __forceinline__ void load_pair(PairW& w, const moe_w4_t& G, const moe_w4_t& U,
                                           size_t row, int H, int lane) {
   const int c = lane < (H >> 5) ? lane : (H >> 5) - 1;
   const size_t sidx = row * (size_t)(H >> 6) + (c >> 1);
-  w.g = load_once(G.q + row * (size_t)(H >> 3) + 4 * c);
-  w.u = load_once(U.q + row * (size_t)(H >> 3) + 4 * c);
-  w.gs = G.scale[sidx];
-  w.gb = G.bias[sidx];
-  w.us = U.scale[sidx];
-  w.ub = U.bias[sidx];
+  if constexpr (NT) {
+    w.g = load_nt(G.q + row * (size_t)(H >> 3) + 4 * c);
+    w.u = load_nt(U.q + row * (size_t)(H >> 3) + 4 * c);
+    w.gs = __builtin_nontemporal_load(G.scale + sidx);
+    w.gb = __builtin_nontemporal_load(G.bias + sidx);
+    w.us = __builtin_nontemporal_load(U.scale + sidx);
+    w.ub = __builtin_nontemporal_load(U.bias + sidx);
+  } else {
+    w.g = reinterpret_cast<const uint4*>(G.q + row * (size_t)(H >> 3))[c];
+    w.u = reinterpret_cast<const uint4*>(U.q + row * (size_t)(H >> 3))[c];
+    w.gs = G.scale[sidx];
+    w.gb = G.bias[sidx];
+    w.us = U.scale[sidx];
+    w.ub = U.bias[sidx];
+  }
 }
 
 // Partial gate and up dot products of the lane's chunk with the m tokens listed in tok (token
@@ -361,7 +368,7 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
         w[i] = j < n4 ? reinterpret_cast<const float4*>(wrow)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     } else if (shared_task) {
-      load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
+      load_pair<false>(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
     }
   };
   if (p.rin) {
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(256) void k_dec_a(DecodeArgs p) {
       }
       store_x();
     } else if (shared_task) {
-      load_pair(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
+      load_pair<false>(pw, p.sh_gate, p.sh_up, (size_t)f, H, lane);
       store_x();
     } else {
       store_x();
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(64 * kDecBWaves) void k_dec_b(DecodeArgs p) {
     for (int b = 0; b < kPB; ++b) {
       const int tk = t0 + b * NW;
       if (b == 0 || tk < nB)  // uniform over the wave; t0 < nB at every call
-        load_pair(w[b], p.gate, p.up, (size_t)expert_of(task_d(tk)) * F + task_f(tk), H, lane);
+        load_pair<true>(w[b], p.gate, p.up, (size_t)expert_of(task_d(tk)) * F + task_f(tk), H, lane);
     }
   };
   auto run = [&](const PairW (&w)[kPB], int t0) {
@@ -672,9 +679,11 @@ __global__ __launch_bounds__(1024) void k_dec_c(DecodeArgs p) {
         const int h = h0 + 4 * r;
         const size_t row = sh ? (size_t)h : (size_t)R.ent_e[d] * H + h;
         const size_t g = row * (size_t)(Kd >> 6) + (c >> 1);
-        bt.w[b][r].q = load_once(q + row * (size_t)(Kd >> 3) + 4 * c);
-        bt.w[b][r].s = sp[g];
-        bt.w[b][r].b = bp[g];
+        // non-temporal for every entry: the shared expert's rows are a small part of the
+        // bytes, and one kind of load keeps the entry's loads free of a branch
+        bt.w[b][r].q = load_nt(q + row * (size_t)(Kd >> 3) + 4 * c);
+        bt.w[b][r].s = __builtin_nontemporal_load(sp + g);
+        bt.w[b][r].b = __builtin_nontemporal_load(bp + g);
       }
       if constexpr (TC == 1) {
         const uint16_t* ar = sh ? p.b.a + (size_t)TK * F : p.b.a + (size_t)R.ent_row0[d] * F;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * kHeadWaves) void k_head_logits(HeadArgs a) {
     if constexpr (WPL >= 4) {
 #pragma unroll
       for (int i = 0; i < WPL / 4; ++i) {
-        const uint4 u = reinterpret_cast<const uint4*>(q)[i];
+        const uint4 u = load_nt(q + 4 * i);
         r.w[4 * i] = u.x; r.w[4 * i + 1] = u.y; r.w[4 * i + 2] = u.z; r.w[4 * i + 3] = u.w;
       }
     } else if constexpr (WPL == 2) {
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(64 * kHeadWaves) void k_head_logits(HeadArgs a) {
     } else {
       r.w[0] = q[0];
     }
-    r.s = a.head.scale[(size_t)v * gpr + g];
-    r.b = a.head.bias[(size_t)v * gpr + g];
+    r.s = __builtin_nontemporal_load(a.head.scale + (size_t)v * gpr + g);
+    r.b = __builtin_nontemporal_load(a.head.bias + (size_t)v * gpr + g);
   };
   float best[TC];
   int bidx[TC];
